@@ -1,0 +1,149 @@
+/*
+ * ssm_oracle.c -- plain fp64 CPU oracle for the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference the GPU kernels are
+ * checked against.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header, table or helper
+ * with the HIP library, and it is never a fallback for it.
+ *
+ * Sources (the pages this follows; page titles as printed on them):
+ *  [xw]  "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ *        (ai.xwebgame.com/papers/mamba), section on what an SSM is: the pair
+ *        h_t = A h_{t-1} + B x_t, y_t = C h_t + D x_t.
+ *  [fs]  fsdata.site article "mamba-state-space-model", section 3.2: the
+ *        selective step -- dt = softplus(.), A_bar = exp(dt*A),
+ *        B_bar = dt*B, h_new = A_bar*h + B_bar*x, y = C.h_new + D*x.
+ *  [fg]  "Mamba: 基于选择状态空间的线性时间序列模型" (freeguideonline.com),
+ *        section 2.2 (ZOH discretisation), section 4.2 step 2 (softplus with
+ *        a bias inside), section 4.3 (channels are independent SSMs),
+ *        section 5.1 (the scan reproduces the sequential recurrence).
+ *  [xw-code] same page as [xw], "run it with PyTorch" section: the block
+ *        gates the SSM output by SiLU of the second projection branch.
+ *
+ * What is computed (per batch b, channel d, state n; all in double):
+ *   x      = delta[b,d,t] + bias[d]
+ *   dt     = softplus(x) = max(x,0) + log1p(exp(-|x|))
+ *   Abar   = exp(dt * A[d,n])
+ *   Bbar   = dt * B[b,n,t]                       (default)
+ *          = (exp(dt*A) - 1) / A * B[b,n,t]      (ZOH flag; dt*B when A == 0)
+ *   h[n]   = Abar * h[n] + Bbar * u[b,d,t]
+ *   y      = sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]   (h after the update)
+ *   out    = y * z / (1 + exp(-z))               (when z is given)
+ *   final_state[b,d,n] = h after the last processed step.
+ * With the REVERSE flag, t runs from L-1 down to 0 (a backward-in-time SSM).
+ * The initial state is zero unless h0 is given.
+ *
+ * Layouts (row-major, contiguous):
+ *   u, delta, z, out : [Bsz, Dm, L]     B, C : [Bsz, N, L]
+ *   A : [Dm, N]   D, bias : [Dm]   h0, final_state : [Bsz, Dm, N]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_ZOH 1
+#define ORACLE_REVERSE 2
+
+static double softplus_f64(double x) {
+  /* stable form of log(1 + exp(x)) */
+  return (x > 0 ? x : 0.0) + log1p(exp(-fabs(x)));
+}
+
+static double silu_f64(double z) { return z / (1.0 + exp(-z)); }
+
+int oracle_abi_version(void) { return 2; }
+
+/* Returns 0 on success, -1 on bad arguments. nthreads <= 0 uses the OpenMP default. */
+int oracle_scan_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
+                    const double* u, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dv,
+                    const double* z, const double* bias, const double* h0,
+                    double* out, double* final_state, int flags, int nthreads) {
+  if (Bsz < 0 || Dm < 0 || N <= 0 || L < 0) return -1;
+  if (!u || !delta || !A || !Bm || !Cm || !out) return -1;
+  const int64_t rows = Bsz * Dm;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t b = r / Dm, d = r % Dm;
+    double* h = (double*)malloc((size_t)N * sizeof(double));
+    if (!h) { bad = 1; continue; }
+    for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[r * N + n] : 0.0;
+    const double* ur = u + r * L;
+    const double* dr = delta + r * L;
+    const double* zr = z ? z + r * L : NULL;
+    double* yr = out + r * L;
+    const double* Ab = Bm + b * N * L;
+    const double* Cb = Cm + b * N * L;
+    for (int64_t s = 0; s < L; ++s) {
+      const int64_t t = (flags & ORACLE_REVERSE) ? (L - 1 - s) : s;
+      const double dt = softplus_f64(dr[t] + (bias ? bias[d] : 0.0));
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double a_dn = A[d * N + n];
+        const double abar = exp(dt * a_dn);
+        double bbar;
+        if ((flags & ORACLE_ZOH) && a_dn != 0.0)
+          bbar = (abar - 1.0) / a_dn * Ab[n * L + t];
+        else
+          bbar = dt * Ab[n * L + t];
+        h[n] = abar * h[n] + bbar * ur[t];
+        acc += Cb[n * L + t] * h[n];
+      }
+      double y = acc + (Dv ? Dv[d] : 0.0) * ur[t];
+      if (zr) y *= silu_f64(zr[t]);
+      yr[t] = y;
+    }
+    if (final_state)
+      for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n];
+    free(h);
+  }
+  return bad ? -1 : 0;
+}
+
+/* One generation step: the scan body with L = 1, state read and written in place.
+ * u, delta, z, out : [Bsz, Dm]; B, C : [Bsz, N]; state : [Bsz, Dm, N]. */
+int oracle_step_f64(int64_t Bsz, int64_t Dm, int64_t N, double* state,
+                    const double* u, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dv,
+                    const double* z, const double* bias, double* out, int flags,
+                    int nthreads) {
+  if (Bsz < 0 || Dm < 0 || N <= 0 || !state || !u || !delta || !A || !Bm || !Cm || !out)
+    return -1;
+  const int64_t rows = Bsz * Dm;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t b = r / Dm, d = r % Dm;
+    const double dt = softplus_f64(delta[r] + (bias ? bias[d] : 0.0));
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a_dn = A[d * N + n];
+      const double abar = exp(dt * a_dn);
+      double bbar;
+      if ((flags & ORACLE_ZOH) && a_dn != 0.0)
+        bbar = (abar - 1.0) / a_dn * Bm[b * N + n];
+      else
+        bbar = dt * Bm[b * N + n];
+      double* h = state + r * N + n;
+      *h = abar * *h + bbar * u[r];
+      acc += Cm[b * N + n] * *h;
+    }
+    double y = acc + (Dv ? Dv[d] : 0.0) * u[r];
+    if (z) y *= silu_f64(z[r]);
+    out[r] = y;
+  }
+  return 0;
+}

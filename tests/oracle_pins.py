@@ -1,0 +1,312 @@
+"""Pins for the fp64 oracle: each check is an independent route to a value the
+pages and the mathematics fix.  None of these re-use the oracle's loop.
+
+Every check takes an oracle object (``.scan`` / ``.step``) and raises
+AssertionError on a mismatch, so the same checks can be run against mutated
+copies of the oracle to show that they catch plausible mistakes.
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.signal
+import scipy.special
+
+RTOL = 1e-12
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / scale)
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)          # library route, independent of log1p(exp(-|x|))
+
+
+def _silu(z):
+    return z * scipy.special.expit(z)
+
+
+def tiny_inputs(seed, Bsz=2, Dm=3, N=4, L=40, gate=True, skip=True, bias=True, h0=False):
+    rng = np.random.default_rng(seed)
+    inp = dict(
+        u=rng.standard_normal((Bsz, Dm, L)),
+        delta=0.5 * rng.standard_normal((Bsz, Dm, L)),
+        A=-rng.uniform(0.2, 3.0, (Dm, N)),
+        B=rng.standard_normal((Bsz, N, L)),
+        C=rng.standard_normal((Bsz, N, L)),
+        D=rng.standard_normal(Dm) if skip else None,
+        z=rng.standard_normal((Bsz, Dm, L)) if gate else None,
+        delta_bias=rng.uniform(-3.0, 0.5, Dm) if bias else None,
+    )
+    if h0:
+        inp["h0"] = rng.standard_normal((Bsz, Dm, N))
+    return inp
+
+
+def brute_force(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, product="prod"):
+    """Unrolled sums: h_t = sum_{s<=t} (prod_{r=s+1..t} Abar_r) Bbar_s u_s (+ prod_{r<=t} Abar_r h0),
+    y_t = C_t . h_t + D u_t, out_t = y_t * silu(z_t).  product='prod' multiplies the Abar
+    factors one by one, product='sum' uses exp(A * sum of dt)."""
+    Bsz, Dm, L = u.shape
+    N = A.shape[1]
+    out = np.zeros((Bsz, Dm, L))
+    hL = np.zeros((Bsz, Dm, N))
+    for b in range(Bsz):
+        for d in range(Dm):
+            x = delta[b, d] + (delta_bias[d] if delta_bias is not None else 0.0)
+            dt = _softplus(x)
+            abar = np.exp(np.outer(dt, A[d]))            # [L, N]
+            bbar = dt[:, None] * B[b].T                  # [L, N]
+            cum = np.concatenate([[0.0], np.cumsum(dt)])
+            for t in range(L):
+                h = np.zeros(N)
+                for s in range(t + 1):
+                    if product == "prod":
+                        w = np.prod(abar[s + 1:t + 1], axis=0)
+                    else:
+                        w = np.exp(A[d] * (cum[t + 1] - cum[s + 1]))
+                    h += w * bbar[s] * u[b, d, s]
+                if h0 is not None:
+                    w0 = np.prod(abar[:t + 1], axis=0) if product == "prod" else np.exp(A[d] * cum[t + 1])
+                    h += w0 * h0[b, d]
+                y = float(C[b, :, t] @ h)
+                if D is not None:
+                    y += D[d] * u[b, d, t]
+                if z is not None:
+                    y *= _silu(z[b, d, t])
+                out[b, d, t] = y
+                if t == L - 1:
+                    hL[b, d] = h
+    return out, hL
+
+
+# ---------------------------------------------------------------- the checks
+
+def check_brute_force(orc):
+    for seed, kw in [(1, {}), (2, dict(gate=False)), (3, dict(skip=False, bias=False)),
+                     (4, dict(N=1, L=17)), (5, dict(Bsz=1, Dm=1, N=3, L=64))]:
+        inp = tiny_inputs(seed, **kw)
+        y, h = orc.scan(**inp)
+        for prod in ("prod", "sum"):
+            yb, hb = brute_force(**inp, product=prod)
+            assert rel(y, yb) < 1e-11, ("brute force y", seed, prod, rel(y, yb))
+            assert rel(h, hb) < 1e-11, ("brute force state", seed, prod, rel(h, hb))
+
+
+def check_initial_state(orc):
+    inp = tiny_inputs(11, h0=True)
+    y, h = orc.scan(**inp)
+    yb, hb = brute_force(**inp)
+    assert rel(y, yb) < 1e-11 and rel(h, hb) < 1e-11
+    # chunking over calls: scan(x[:L1]) then scan(x[L1:], h0 = its final state) == scan(x)
+    inp = tiny_inputs(12, L=50)
+    y, h = orc.scan(**inp)
+    L1 = 23
+    cut = lambda k, sl: {key: (v[..., sl] if key in ("u", "delta", "z", "B", "C") and v is not None else v)
+                         for key, v in inp.items()}
+    y1, h1 = orc.scan(**cut(None, slice(0, L1)))
+    y2, h2 = orc.scan(**cut(None, slice(L1, None)), h0=h1)
+    assert rel(np.concatenate([y1, y2], -1), y) < 1e-13 and rel(h2, h) < 1e-13
+
+
+def check_lti_closed_form(orc):
+    """Constant dt, B, C: y = silu(z) * (K * u + D u) with K_k = sum_n C[n] Abar[n]^k dtB[n]."""
+    rng = np.random.default_rng(21)
+    Dm, N, L = 3, 5, 120
+    A = -rng.uniform(0.1, 2.0, (Dm, N))
+    dl = rng.standard_normal(Dm) * 0.5
+    bias = rng.uniform(-2, 0, Dm)
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    u = rng.standard_normal((1, Dm, L))
+    z = rng.standard_normal((1, Dm, L))
+    Dv = rng.standard_normal(Dm)
+    inp = dict(u=u, delta=np.repeat(dl[None, :, None], L, -1), A=A,
+               B=np.repeat(Bc[None, :, None], L, -1), C=np.repeat(Cc[None, :, None], L, -1),
+               D=Dv, z=z, delta_bias=bias)
+    y, h = orc.scan(**inp)
+    for d in range(Dm):
+        dt = _softplus(dl[d] + bias[d])
+        abar = np.exp(dt * A[d])
+        k = np.arange(L)
+        K = (Cc[None, :] * abar[None, :] ** k[:, None] * (dt * Bc)[None, :]).sum(1)
+        conv1 = np.convolve(u[0, d], K)[:L]
+        conv2 = scipy.signal.fftconvolve(u[0, d], K)[:L]
+        hs = np.stack([scipy.signal.lfilter([dt * Bc[n]], [1.0, -abar[n]], u[0, d]) for n in range(N)])
+        conv3 = Cc @ hs
+        for ref in (conv1, conv2, conv3):
+            ref_y = (ref + Dv[d] * u[0, d]) * _silu(z[0, d])
+            assert rel(y[0, d], ref_y) < 1e-10, rel(y[0, d], ref_y)
+        assert rel(h[0, d], hs[:, -1]) < 1e-12
+        # impulse response h_t = Abar^t dt B u_0
+        imp = dict(inp)
+        imp["u"] = np.zeros_like(u)
+        imp["u"][0, :, 0] = 1.0
+        imp["z"] = None
+        imp["D"] = None
+    yi, _ = orc.scan(**imp)
+    for d in range(Dm):
+        dt = _softplus(dl[d] + bias[d])
+        abar = np.exp(dt * A[d])
+        t = np.arange(L)
+        expect = (Cc[None, :] * np.exp(np.outer(t, dt * A[d])) * (dt * Bc)[None, :]).sum(1)
+        assert rel(yi[0, d], expect) < 1e-12
+
+
+def check_zoh_library(orc):
+    """Exact ZOH B_bar against scipy.signal.cont2discrete on a constant (LTI) diagonal system."""
+    rng = np.random.default_rng(31)
+    N, L = 4, 60
+    A = -rng.uniform(0.1, 2.0, (1, N))
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    dl, bias = 0.3, -0.7
+    u = rng.standard_normal((1, 1, L))
+    y, h = orc.scan(u, np.full((1, 1, L), dl), A, np.repeat(Bc[None, :, None], L, -1),
+                    np.repeat(Cc[None, :, None], L, -1), D=np.array([0.5]), delta_bias=np.array([bias]),
+                    zoh=True)
+    dt = _softplus(dl + bias)
+    Ad, Bd, Cd, Dd, _ = scipy.signal.cont2discrete((np.diag(A[0]), Bc[:, None], Cc[None, :],
+                                                    np.array([[0.5]])), dt, method="zoh")
+    # y_k = C x_k + D u_k with x_k = Ad x_{k-1} + Bd u_k  (state read after the update)
+    x = np.zeros(N)
+    ref = np.zeros(L)
+    for k in range(L):
+        x = Ad @ x + Bd[:, 0] * u[0, 0, k]
+        ref[k] = Cd[0] @ x + Dd[0, 0] * u[0, 0, k]
+    assert rel(y[0, 0], ref) < 1e-10, rel(y[0, 0], ref)
+    # A -> 0 limit of ZOH is the Euler B_bar = dt * B
+    inp = tiny_inputs(32)
+    inp["A"] = np.zeros_like(inp["A"])
+    y1, _ = orc.scan(**inp, zoh=True)
+    y2, _ = orc.scan(**inp, zoh=False)
+    assert rel(y1, y2) == 0.0
+
+
+def check_a_zero_cumsum(orc):
+    inp = tiny_inputs(41, gate=False, skip=False)
+    inp["A"] = np.zeros_like(inp["A"])
+    y, h = orc.scan(**inp)
+    for b in range(2):
+        for d in range(3):
+            dt = _softplus(inp["delta"][b, d] + inp["delta_bias"][d])
+            hs = np.cumsum(dt[:, None] * inp["B"][b].T * inp["u"][b, d][:, None], axis=0)  # [L, N]
+            assert rel(h[b, d], hs[-1]) < 1e-13
+            assert rel(y[b, d], (inp["C"][b].T * hs).sum(1)) < 1e-12
+
+
+def check_small_step_skip(orc):
+    """dt -> 0 (bias -40): y = D u silu(z), and y = D u without a gate."""
+    inp = tiny_inputs(51)
+    inp["delta_bias"] = np.full(3, -40.0)
+    y, h = orc.scan(**inp)
+    ref = inp["D"][None, :, None] * inp["u"] * _silu(inp["z"])
+    assert rel(y, ref) < 1e-14 and np.max(np.abs(h)) < 1e-15
+    inp["z"] = None
+    y, _ = orc.scan(**inp)
+    assert rel(y, inp["D"][None, :, None] * inp["u"]) < 1e-14
+
+
+def check_single_step_closed_form(orc):
+    rng = np.random.default_rng(61)
+    for with_h0 in (False, True):
+        inp = tiny_inputs(62 + with_h0, L=1, h0=with_h0)
+        y, h = orc.scan(**inp)
+        dt = _softplus(inp["delta"][..., 0] + inp["delta_bias"][None, :])        # [B, D]
+        h_exp = dt[..., None] * inp["B"][:, None, :, 0] * inp["u"][..., 0][..., None]
+        if with_h0:
+            h_exp = h_exp + np.exp(dt[..., None] * inp["A"][None]) * inp["h0"]
+        assert rel(h, h_exp) < 1e-14
+        y_exp = ((h_exp * inp["C"][:, None, :, 0]).sum(-1) + inp["D"][None] * inp["u"][..., 0]) \
+            * _silu(inp["z"][..., 0])
+        assert rel(y[..., 0], y_exp) < 1e-14
+    del rng
+
+
+def check_step_matches_scan(orc):
+    inp = tiny_inputs(71, L=20)
+    y, h = orc.scan(**inp)
+    st = np.zeros((2, 3, 4))
+    for t in range(20):
+        yt, st = orc.step(st, inp["u"][..., t], inp["delta"][..., t], inp["A"], inp["B"][..., t],
+                          inp["C"][..., t], D=inp["D"], z=inp["z"][..., t], delta_bias=inp["delta_bias"])
+        assert rel(yt, y[..., t]) < 1e-14
+    assert rel(st, h) < 1e-14
+
+
+def check_softplus_silu(orc):
+    """Through the oracle: N=1, A=0, B=C=u=1, D=0, L=1 gives y = softplus(delta + bias);
+    B=0, D=u=1 gives y = silu(z)."""
+    x = np.concatenate([np.linspace(-50, 50, 201), [0.0, 1e-8, -1e-8, 700.0, -700.0]])
+    M = x.size
+    one = np.ones((1, M, 1))
+    y, _ = orc.scan(one, x.reshape(1, M, 1), np.zeros((M, 1)), np.ones((1, 1, 1)), np.ones((1, 1, 1)))
+    sp = y[0, :, 0]
+    assert rel(sp, _softplus(x)) < 1e-15
+    assert np.max(np.abs(sp[:201] - sp[:201][::-1] - x[:201])) < 1e-12   # softplus(x) - softplus(-x) = x
+    assert abs(sp[201] - np.log(2.0)) < 1e-16
+    y, _ = orc.scan(one, np.zeros((1, M, 1)), np.zeros((M, 1)), np.zeros((1, 1, 1)), np.ones((1, 1, 1)),
+                    D=np.ones(M), z=x.reshape(1, M, 1))
+    si = y[0, :, 0]
+    assert rel(si[:201], x[:201] * scipy.special.expit(x[:201])) < 1e-15
+    assert np.max(np.abs(si[:201] - si[:201][::-1] - x[:201])) < 1e-12    # silu(z) - silu(-z) = z
+    assert si[201] == 0.0
+
+
+def check_linearity_in_u(orc):
+    inp = tiny_inputs(81)
+    rng = np.random.default_rng(82)
+    u2 = rng.standard_normal(inp["u"].shape)
+    a, b = 0.7, -1.3
+    y1, h1 = orc.scan(**inp)
+    y2, h2 = orc.scan(**{**inp, "u": u2})
+    y3, h3 = orc.scan(**{**inp, "u": a * inp["u"] + b * u2})
+    assert rel(y3, a * y1 + b * y2) < 1e-12 and rel(h3, a * h1 + b * h2) < 1e-12
+
+
+def check_causality(orc):
+    inp = tiny_inputs(91, L=30)
+    y, _ = orc.scan(**inp)
+    for s in (0, 7, 29):
+        pert = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+        for key in ("u", "delta", "z", "B", "C"):
+            pert[key][..., s] += 1.5
+        yp, _ = orc.scan(**pert)
+        assert np.array_equal(yp[..., :s], y[..., :s])
+        assert not np.allclose(yp[..., s], y[..., s])
+
+
+def check_reverse(orc):
+    inp = tiny_inputs(101)
+    y, h = orc.scan(**inp, reverse=True)
+    flip = {k: (v[..., ::-1].copy() if k in ("u", "delta", "z", "B", "C") else v) for k, v in inp.items()}
+    yf, hf = orc.scan(**flip)
+    assert rel(y, yf[..., ::-1]) < 1e-15 and rel(h, hf) < 1e-15
+    yb, _ = brute_force(**flip)
+    assert rel(y, yb[..., ::-1]) < 1e-11
+
+
+def check_permutation_equivariance(orc):
+    inp = tiny_inputs(111, Bsz=3, Dm=5)
+    y, h = orc.scan(**inp)
+    pd = np.array([3, 0, 4, 1, 2])
+    pb = np.array([2, 0, 1])
+    p = dict(inp)
+    for k in ("u", "delta", "z"):
+        p[k] = inp[k][pb][:, pd]
+    for k in ("B", "C"):
+        p[k] = inp[k][pb]
+    p["A"] = inp["A"][pd]
+    p["D"] = inp["D"][pd]
+    p["delta_bias"] = inp["delta_bias"][pd]
+    yp, hp = orc.scan(**p)
+    assert np.array_equal(yp, y[pb][:, pd]) and np.array_equal(hp, h[pb][:, pd])
+
+
+ALL_CHECKS = [check_brute_force, check_initial_state, check_lti_closed_form, check_zoh_library,
+              check_a_zero_cumsum, check_small_step_skip, check_single_step_closed_form,
+              check_step_matches_scan, check_softplus_silu, check_linearity_in_u, check_causality,
+              check_reverse, check_permutation_equivariance]

@@ -1,0 +1,53 @@
+"""Plant plausible mistakes in a temporary copy of the oracle source and check
+that at least one pin fails for each (CPU only).  The oracle itself is untouched."""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("drop_D_skip", "double y = acc + (Dv ? Dv[d] : 0.0) * ur[t];", "double y = acc;"),
+    ("y_from_old_state",
+     "h[n] = abar * h[n] + bbar * ur[t];\n        acc += Cb[n * L + t] * h[n];",
+     "acc += Cb[n * L + t] * h[n];\n        h[n] = abar * h[n] + bbar * ur[t];"),
+    ("sign_of_A", "const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab",
+     "const double abar = exp(-dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab"),
+    ("bias_outside_softplus", "softplus_f64(dr[t] + (bias ? bias[d] : 0.0))",
+     "(softplus_f64(dr[t]) + (bias ? bias[d] : 0.0))"),
+    ("B_transposed", "bbar = dt * Ab[n * L + t];", "bbar = dt * Ab[t * N + n];"),
+    ("softplus_missing_abs", "log1p(exp(-fabs(x)))", "log1p(exp(-x))"),
+    ("silu_sign", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    ("D_outside_gate",
+     "double y = acc + (Dv ? Dv[d] : 0.0) * ur[t];\n      if (zr) y *= silu_f64(zr[t]);",
+     "double y = acc;\n      if (zr) y *= silu_f64(zr[t]);\n      y += (Dv ? Dv[d] : 0.0) * ur[t];"),
+    ("input_u_dropped", "h[n] = abar * h[n] + bbar * ur[t];", "h[n] = abar * h[n] + bbar;"),
+    ("C_off_by_one", "acc += Cb[n * L + t] * h[n];", "acc += Cb[n * L + (t > 0 ? t - 1 : 0)] * h[n];"),
+    ("initial_state_ignored", "h[n] = h0 ? h0[r * N + n] : 0.0;", "h[n] = 0.0;"),
+    ("reverse_ignored", "(flags & ORACLE_REVERSE) ? (L - 1 - s) : s", "s"),
+    ("zoh_sign", "bbar = (abar - 1.0) / a_dn * Ab[n * L + t];", "bbar = (1.0 - abar) / a_dn * Ab[n * L + t];"),
+    ("step_drops_u", "*h = abar * *h + bbar * u[r];", "*h = abar * *h + bbar;"),
+    ("A_transposed", "const double a_dn = A[d * N + n];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab",
+     "const double a_dn = A[n * Dm + d];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab"),
+    ("state_written_before_last_step", "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n];",
+     "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n] * 0.5;"),
+    ("step_bias_dropped", "const double dt = softplus_f64(delta[r] + (bias ? bias[d] : 0.0));",
+     "const double dt = softplus_f64(delta[r]);"),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, orig, mut):
+    src = oracle.source()
+    assert src.count(orig) == 1, "mutation anchor must occur exactly once: " + name
+    path = oracle.compile_variant(src.replace(orig, mut), os.path.join(str(tmp_path), "mut_%s.so" % name))
+    bad = oracle.Oracle(path)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(bad)
+        except (AssertionError, FloatingPointError, ValueError, RuntimeError):
+            caught.append(check.__name__)
+    assert caught, "no pin caught mutant " + name
