@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X selective scan (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba130m]
+
+A step is one ssm_scan_fwd call over a whole batch of the workload (discretise,
+scan, carry, output epilogue: the entire prefill/training-forward path) with
+every input already resident in HBM.  The timed loop rotates through enough
+independent input sets that they cannot be served from the 256 MB Infinity
+Cache.  The same JSON line also carries the decode path (ssm_state_update) on
+the 2.8B-shaped generation workload and the fp64 CPU oracle's rate on the host.
+
+Progress goes to stderr; stdout gets exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "selective-scan state updates/sec (B·L·D·N) and HBM GB/s % of peak, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+# VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (non-packed fp32 lane-ops per second)
+VALU_PEAK_TLANE = 256 * 64 * 2.4e9 / 1e12
+# algorithmic VALU issue slots per state update: exp2 argument (mul), v_exp_f32 (2 slots: it issues
+# at half the FMA rate on gfx950, measured), B_bar*u (mul), h update (FMA), C*h (FMA)
+SLOTS_PER_UPDATE = 6
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "selective_state_space_76_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def scan_bytes(w) -> int:
+    """Algorithmic HBM bytes of one scan call: each input read once, each output written once."""
+    s = 4 if w.io == "f32" else 2
+    BDL, BNL = w.batch * w.dim * w.seqlen, w.batch * w.dstate * w.seqlen
+    return (3 * s * BDL + s * BDL + 2 * s * BNL + 4 * w.dim * w.dstate + 4 * w.dim * (2 if w.bias else 1)
+            + 4 * w.batch * w.dim * w.dstate)
+
+
+def step_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode step: state read + written, per-token streams, params."""
+    s = 4 if w.io == "f32" else 2
+    BD, BDN = w.batch * w.dim, w.batch * w.dim * w.dstate
+    return 2 * 4 * BDN + 4 * s * BD + 2 * s * w.batch * w.dstate + 4 * w.dim * w.dstate + 8 * w.dim
+
+
+def traffic_from_profile(workload: str, launches_per_call: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this build."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def bench_scan(args, torch, ssm, W):
+    w = W.WORKLOADS[args.workload]
+    per_set = scan_bytes(w)
+    R = max(1, min(8, math.ceil(2 * MALL_BYTES / per_set)))
+    log("workload %s %s, %d rotated input sets of %.1f MB" % (w.name, (w.batch, w.dim, w.dstate, w.seqlen),
+                                                                R, per_set / 1e6))
+    sets = []
+    for k in range(R):
+        x = W.scan_inputs(w.with_shape(seed=w.seed + 1000 * k), device="cuda")
+        x["out"] = torch.empty_like(x["u"])
+        x["fs"] = torch.empty(w.batch, w.dim, w.dstate, device="cuda")
+        sets.append(x)
+    need = ssm.workspace_size(w.batch, w.dim, w.dstate, w.seqlen, ssm.SSM_BF16 if w.io == "bf16" else ssm.SSM_F32)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+
+    def call(x):
+        ssm.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                     out=x["out"], final_state=x["fs"], workspace=ws)
+
+    for k in range(args.warmup):
+        call(sets[k % R])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        call(sets[k % R])
+        ends[k].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    return w, R, ms_step, mean_launch, launch_ms, sets[0]
+
+
+def bench_decode(args, torch, ssm, W):
+    w = W.WORKLOADS["decode2p8b"]
+    steps = args.decode_steps
+    A, Dv, bias = W.params(w, device="cuda")
+    nstate = max(1, math.ceil(1.25 * MALL_BYTES / (4 * w.batch * w.dim * w.dstate)))
+    states = [torch.zeros(w.batch, w.dim, w.dstate, device="cuda") for _ in range(nstate)]
+    log("decode %s x %d steps, %d rotated state buffers" % ((w.batch, w.dim, w.dstate), steps, nstate))
+    inputs = [W.decode_inputs(w, k, device="cuda") for k in range(steps)]
+    outs = [torch.empty(w.batch, w.dim, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+    def step(k):
+        x = inputs[k]
+        ssm.state_update(states[k % nstate], x["u"], x["delta"], A, x["B"], x["C"], Dv, x["z"], bias,
+                         out=outs[k % 2])
+
+    for k in range(min(20, steps)):
+        step(k)
+    for s in states:
+        s.zero_()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for k in range(steps):
+        step(k)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+    ms_step = (t1 - t0) * 1e3 / steps
+    gpu_ms = ev[0].elapsed_time(ev[steps]) / steps
+    upd = w.batch * w.dim * w.dstate
+    b = step_bytes(w)
+    return {
+        "workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "steps": steps,
+        "rotated_state_buffers": nstate,
+        "value": upd / (ms_step * 1e-3), "unit": "state-updates/s", "ms_per_step": ms_step,
+        "gpu_ms_per_step": gpu_ms, "median_step_ms": per[len(per) // 2],
+        "hbm": {"bound": "hbm", "achieved": b / (gpu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": b / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_step": b},
+    }
+
+
+def cpu_baseline(torch, x, w, seconds):
+    """The fp64 oracle as it stands, on this host's cores, over the same inputs (repeated to ~seconds)."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import oracle
+
+    host = {k: (None if v is None else np.ascontiguousarray(v.detach().to("cpu", torch.float64).numpy()))
+            for k, v in x.items() if k not in ("out", "fs")}
+    B_rows = w.batch
+    upd = 0
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        oracle.scan(host["u"], host["delta"], host["A"], host["B"], host["C"], D=host["D"], z=host["z"],
+                    delta_bias=host["delta_bias"])
+        upd += w.batch * w.dim * w.dstate * w.seqlen
+        runs += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "%d full pass(es) of the %s workload (%d x %d x %d x %d, the same bf16 inputs widened "
+                      "to fp64), %.1f s wall" % (runs, w.name, B_rows, w.dim, w.dstate, w.seqlen, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba130m", choices=["mamba130m", "mamba1p3b", "dna1m", "tiny"])
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan shards over (batch, channel) with no exchange, so "
+              "a multi-GPU figure is not produced by this build (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, ROOT)
+    import selective_state_space_76_amd as ssm
+    from selective_state_space_76_amd import workloads as W
+    ssm.load()
+
+    w, R, ms_step, launch_ms, all_launch, x0 = bench_scan(args, torch, ssm, W)
+    upd = w.updates
+    b = scan_bytes(w)
+    value = upd / (ms_step * 1e-3)
+    alu = upd * SLOTS_PER_UPDATE / (launch_ms * 1e-3) / 1e12
+    gbs = b / (launch_ms * 1e-3) / 1e9
+    log("scan: %.4f ms/step (wall), %.4f ms/launch (events) -> %.3e updates/s, %.1f GB/s"
+        % (ms_step, launch_ms, value, gbs))
+    res = {
+        "metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen,
+                   "io_dtype": w.io, "state_dtype": "f32", "rotated_input_sets": R},
+        "roofline": {"bound": "alu", "achieved": alu, "peak": VALU_PEAK_TLANE, "unit": "T VALU lane-slots/s",
+                     "frac": alu / VALU_PEAK_TLANE, "traffic": traffic_from_profile(w.name, 1),
+                     "slots_per_update": SLOTS_PER_UPDATE, "launch_ms": launch_ms,
+                     "launch_ms_median": all_launch[len(all_launch) // 2]},
+        "hbm": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes_per_launch": b},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_decode:
+        d = bench_decode(args, torch, ssm, W)
+        log("decode: %.4f ms/step wall, %.4f ms/step events, %.1f GB/s" % (d["ms_per_step"], d["gpu_ms_per_step"],
+                                                                          d["hbm"]["achieved"]))
+        res["decode"] = d
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(torch, x0, w, args.cpu_seconds)
+        log("cpu baseline: %.3e updates/s on %d threads" % (res["cpu_baseline"]["value"], res["cpu_baseline"]["cores"]))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan.so, the MI355X (gfx950) selective state-space scan.
+ *
+ * The operation (per batch b, channel d, state n, step t) is the selective SSM
+ * recurrence that the pages describe:
+ *   dt      = softplus(delta[b,d,t] + delta_bias[d])   -- step size from the input,
+ *             bias inside the softplus ("Mamba: 基于选择状态空间的线性时间序列模型",
+ *             freeguideonline.com, section 4.2 step 2; fsdata.site
+ *             "mamba-state-space-model" article, section 3.2)
+ *   A_bar   = exp(dt * A[d,n])                          -- fsdata.site article, section 3.2
+ *   B_bar   = dt * B[b,n,t]                             -- same section (default)
+ *           = (exp(dt*A) - 1) / A * B[b,n,t]            -- exact zero-order hold, with
+ *             SSM_FLAG_ZOH (freeguideonline tutorial, section 2.2)
+ *   h[n]    = A_bar * h[n] + B_bar * u[b,d,t]
+ *   y       = sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]   -- output read from the updated
+ *             state plus the skip term ("Mamba: Linear-Time Sequence Modeling with
+ *             Selective State Spaces", ai.xwebgame.com, section on what an SSM is)
+ *   out     = y * silu(z[b,d,t])                        -- gate by the second branch
+ *             (same page, the PyTorch block's gating step)
+ * Each channel d is an independent SSM with its own diagonal A[d,:]
+ * (freeguideonline tutorial, section 4.3); B and C are shared by all channels of
+ * a batch row.  The scan computes the sequential recurrence exactly up to
+ * floating-point rounding order (freeguideonline tutorial, section 5.1).  The
+ * state is fp32; streams are fp32 or bf16 (rounded to nearest even on output).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller (the library
+ *     allocates nothing and keeps no pointer after returning).  Tensors are
+ *     dense, row-major, with the layouts given below, and every base pointer
+ *     must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Outputs are valid once the stream has been synchronised.
+ *   - Every argument is checked on the host before anything is enqueued; on any
+ *     error nothing is launched and no output is touched.  The return code is
+ *     the only error channel.
+ *   - `out` and `final_state` must not overlap any input (checked: SSM_ERR_OVERLAP).
+ *   - Calls are reentrant; concurrent calls on different streams are safe when
+ *     their output buffers are distinct.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t*` */
+
+typedef enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSM_ERR_SHAPE = 2,       /* a size is out of range (batch/dim/seqlen < 1, dstate not in [1,64]) */
+  SSM_ERR_DTYPE = 3,       /* io_dtype is not SSM_F32 or SSM_BF16 */
+  SSM_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
+  SSM_ERR_UNSUPPORTED = 5, /* unknown flag bits */
+  SSM_ERR_WORKSPACE = 6,   /* workspace non-NULL but smaller than ssm_scan_workspace_size() */
+  SSM_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch (hipGetLastError) */
+  SSM_ERR_OVERLAP = 8      /* an output buffer overlaps an input buffer */
+} ssm_status;
+
+typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* flag bits for ssm_shape.flags / ssm_state_update(flags) */
+#define SSM_FLAG_ZOH 1u     /* exact zero-order-hold B_bar instead of dt*B */
+#define SSM_FLAG_REVERSE 2u /* scan from t = L-1 down to 0 (a backward-in-time SSM;
+                               fsdata.site article, section 7 pitfalls table) */
+
+typedef struct ssm_shape {
+  int64_t batch;   /* B >= 1 */
+  int64_t dim;     /* D (d_inner) >= 1 */
+  int64_t dstate;  /* N in [1, 64] */
+  int64_t seqlen;  /* L >= 1 */
+  int32_t io_dtype;/* ssm_dtype of u, delta, B, C, z and out */
+  uint32_t flags;  /* SSM_FLAG_* bits */
+} ssm_shape;
+
+/* Version of this header's ABI (bumped on any incompatible change). */
+#define SSM_ABI_VERSION 1
+int ssm_abi_version(void);
+
+/* Static string for a status code (never NULL). */
+const char* ssm_status_str(int status);
+
+/* Bytes of device workspace that ssm_scan_fwd may use for this shape to split
+ * long sequences across workgroups (0 when no split is used).  Depends on the
+ * shape only.  Returns 0 for an invalid shape. */
+size_t ssm_scan_workspace_size(const ssm_shape* shape);
+
+/* Selective scan over a whole sequence (prefill / training forward).
+ *   u, delta, z, out : [B, D, L]  io_dtype
+ *   A                : [D, N]     fp32 (the pages use negative reals)
+ *   B, C             : [B, N, L]  io_dtype, shared by all D channels of a batch row
+ *   D, delta_bias    : [D]        fp32, NULL means zero
+ *   z                : NULL means no gate (out = y)
+ *   initial_state    : [B, D, N]  fp32 state before the first processed step,
+ *                      NULL means zero (lets a long sequence be scanned in
+ *                      several calls; mlqm.cn article, section 6.2)
+ *   final_state      : [B, D, N]  fp32 state after the last processed step,
+ *                      NULL means not written
+ *   workspace        : device scratch of workspace_bytes; NULL with 0 bytes runs
+ *                      without splitting the sequence (always correct, slower when
+ *                      batch*dim is small).  Non-NULL but smaller than
+ *                      ssm_scan_workspace_size() is SSM_ERR_WORKSPACE.  The
+ *                      library does not keep it; its contents are not preserved.
+ * With SSM_FLAG_REVERSE the steps run from L-1 to 0; final_state is then the
+ * state after step 0. */
+ssm_status ssm_scan_fwd(const ssm_shape* shape,
+                        const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D,
+                        const void* z, const float* delta_bias,
+                        const float* initial_state,
+                        void* out, float* final_state,
+                        void* workspace, size_t workspace_bytes,
+                        struct ihipStream_t* stream);
+
+/* One recurrent generation step (the scan body with L = 1), state updated in place:
+ * the fixed-size state replaces a growing cache (fsdata.site article, section 3.2
+ * and the comparison table in section 5).
+ *   state            : [B, D, N]  fp32, read and written
+ *   u, delta, z, out : [B, D]     io_dtype
+ *   A                : [D, N]     fp32
+ *   B, C             : [B, N]     io_dtype
+ *   D, delta_bias    : [D]        fp32, NULL means zero; z NULL means no gate
+ * flags: SSM_FLAG_ZOH only. */
+ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t io_dtype,
+                            uint32_t flags, float* state,
+                            const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            void* out, struct ihipStream_t* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -125,6 +125,13 @@ def default() -> Oracle:
     return _default
 
 
+def max_threads() -> int:
+    """Threads the oracle's OpenMP loops use by default."""
+    lib = default().lib
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return int(lib.oracle_max_threads())
+
+
 def scan(*args, **kw):
     return default().scan(*args, **kw)
 

@@ -56,6 +56,15 @@ static double silu_f64(double z) { return z / (1.0 + exp(-z)); }
 
 int oracle_abi_version(void) { return 2; }
 
+/* Threads an OpenMP region of the oracle uses by default (1 without OpenMP). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 /* Returns 0 on success, -1 on bad arguments. nthreads <= 0 uses the OpenMP default. */
 int oracle_scan_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
                     const double* u, const double* delta, const double* A,

@@ -1,0 +1,156 @@
+"""ctypes binding of libssmscan.so (see include/ssm_scan.h).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of the
+library.  There is no fallback: if the library is missing or no GPU is visible,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.so")
+
+SSM_F32 = 0
+SSM_BF16 = 1
+SSM_FLAG_ZOH = 1
+SSM_FLAG_REVERSE = 2
+ABI_VERSION = 1
+
+_STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_ALIGN",
+           5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH", 8: "SSM_ERR_OVERLAP"}
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%d): %s" % (_STATUS.get(status, "?"), status, message))
+        self.status = status
+
+
+class ssm_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update")
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libssmscan.so not found at %s; build it with "
+                          "`python -m selective_state_space_76_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_abi_version.restype = ctypes.c_int
+    lib.ssm_status_str.argtypes = [ctypes.c_int]
+    lib.ssm_status_str.restype = ctypes.c_char_p
+    lib.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ssm_shape)]
+    lib.ssm_scan_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 11 + [vp, ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_state_update.argtypes = [i64, i64, i64, i32, u32] + [vp] * 10 + [vp]
+    lib.ssm_state_update.restype = ctypes.c_int
+    if lib.ssm_abi_version() != ABI_VERSION:
+        raise ImportError("libssmscan.so ABI version %d, binding expects %d" % (lib.ssm_abi_version(), ABI_VERSION))
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SSMError(status, load().ssm_status_str(status).decode())
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError("streams must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a tensor, got %r" % type(t))
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_shape(batch, dim, dstate, seqlen, io_dtype, zoh=False, reverse=False) -> ssm_shape:
+    flags = (SSM_FLAG_ZOH if zoh else 0) | (SSM_FLAG_REVERSE if reverse else 0)
+    return ssm_shape(int(batch), int(dim), int(dstate), int(seqlen), int(io_dtype), flags)
+
+
+def workspace_size(batch, dim, dstate, seqlen, io_dtype=SSM_BF16, zoh=False, reverse=False) -> int:
+    sh = make_shape(batch, dim, dstate, seqlen, io_dtype, zoh, reverse)
+    return int(load().ssm_scan_workspace_size(ctypes.byref(sh)))
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *,
+             out=None, final_state=True, zoh=False, reverse=False, workspace=None, split=True,
+             stream=None):
+    """Selective scan.  u, delta, z: [B,D,L]; B, C: [B,N,L] (same dtype as u); A: [D,N] fp32;
+    D, delta_bias: [D] fp32; initial_state: [B,D,N] fp32 or None.
+    Returns (out [B,D,L] in u's dtype, final_state [B,D,N] fp32 or None).
+    final_state may be True (allocate), False/None (not written) or a tensor to write into.
+    workspace: a uint8 tensor of at least workspace_size(...) bytes, or None to allocate one;
+    split=False runs without a workspace (no sequence split)."""
+    lib = load()
+    Bsz, Dm, L = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
+    if out is None:
+        out = torch.empty_like(u)
+    if final_state is True:
+        final_state = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=u.device)
+    elif final_state is False:
+        final_state = None
+    ws_bytes = 0
+    if split:
+        need = int(lib.ssm_scan_workspace_size(ctypes.byref(sh)))
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+        if workspace is not None:
+            ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
+    _check(lib.ssm_scan_fwd(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                            _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, final_state
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None, zoh=False,
+                 stream=None):
+    """One recurrent step, state [B,D,N] fp32 updated in place.  u, delta, z: [B,D]; B, C: [B,N].
+    Returns out [B,D] in u's dtype."""
+    lib = load()
+    Bsz, Dm = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    if out is None:
+        out = torch.empty_like(u)
+    _check(lib.ssm_state_update(Bsz, Dm, N, io, SSM_FLAG_ZOH if zoh else 0, _ptr(state), _ptr(u), _ptr(delta),
+                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
+                                _stream(stream)))
+    return out

@@ -1,0 +1,218 @@
+// ssm_abi.cpp -- the C entry points declared in include/ssm_scan.h.
+//
+// Every argument is validated on the host before anything is enqueued; no HIP
+// runtime call is made for an invalid call, so the checks can be exercised on
+// a machine without a GPU.  The library allocates no memory and keeps no state.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ssm_scan.h"
+#include "ssm_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+constexpr int64_t kMaxElems = int64_t(1) << 61;
+constexpr int kTargetBlocks = 1024;    // 4 workgroups of 4 waves per CU on 256 CUs
+constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t elems, int64_t esize) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(elems * esize)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a <= 0 || b <= 0) return false;
+  if (a > kMaxElems / b) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Plan {
+  int64_t S = 1, seg_len = 0, nblk = 0;
+  size_t ws_state = 0, ws_dsum = 0, ws_carry = 0, total = 0;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shape-only choice of the sequence split, so results never depend on the device.
+bool make_plan(const ssm_shape* s, Plan* pl) {
+  if (!s) return false;
+  if (s->batch < 1 || s->dim < 1 || s->seqlen < 1 || s->dstate < 1 || s->dstate > 64) return false;
+  if (s->batch > kMaxDim || s->dim > kMaxDim || s->seqlen > kMaxDim) return false;
+  int64_t bd, bdl, bdn;
+  if (!mul_ok(s->batch, s->dim, &bd) || !mul_ok(bd, s->seqlen, &bdl) || !mul_ok(bd, s->dstate, &bdn))
+    return false;
+  int64_t bnl;
+  if (!mul_ok(s->batch * s->dstate, s->seqlen, &bnl)) return false;
+  pl->nblk = (s->dim + 15) / 16;
+  const int64_t base = s->batch * pl->nblk;
+  if (base > (int64_t(1) << 30)) return false;
+  const int64_t L = s->seqlen;
+  pl->S = 1;
+  pl->seg_len = ((L + 63) / 64) * 64;
+  if (base < kTargetBlocks / 2 && L >= 2 * kMinSegment) {
+    const int64_t want = (kTargetBlocks + base - 1) / base;
+    int64_t seg = (L + want - 1) / want;
+    seg = ((seg + 63) / 64) * 64;
+    if (seg < kMinSegment) seg = kMinSegment;
+    const int64_t S = (L + seg - 1) / seg;
+    if (S > 1) {
+      pl->S = S;
+      pl->seg_len = seg;
+    }
+  }
+  if (base * pl->S > (int64_t(1) << 31) - 1) return false;
+  if (pl->S > 1) {
+    pl->ws_state = round256(sizeof(float) * (size_t)(pl->S - 1) * (size_t)bdn);
+    pl->ws_dsum = round256(sizeof(float) * (size_t)(pl->S - 1) * (size_t)bd);
+    pl->ws_carry = round256(sizeof(float) * (size_t)pl->S * (size_t)bdn);
+    pl->total = pl->ws_state + pl->ws_dsum + pl->ws_carry;
+  }
+  return true;
+}
+
+ssm_status launch_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_str(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "a size is out of range (batch, dim, seqlen >= 1; dstate in [1, 64])";
+    case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
+    case SSM_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case SSM_ERR_UNSUPPORTED: return "unknown flag bits";
+    case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_workspace_size()";
+    case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case SSM_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+    default: return "unknown status";
+  }
+}
+
+size_t ssm_scan_workspace_size(const ssm_shape* shape) {
+  Plan pl;
+  if (!make_plan(shape, &pl)) return 0;
+  return pl.total;
+}
+
+ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, const float* initial_state, void* out,
+                        float* final_state, void* workspace, size_t workspace_bytes,
+                        struct ihipStream_t* stream) {
+  if (!shape) return SSM_ERR_NULL;
+  if (shape->io_dtype != SSM_F32 && shape->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (shape->flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE)) return SSM_ERR_UNSUPPORTED;
+  Plan pl;
+  if (!make_plan(shape, &pl)) return SSM_ERR_SHAPE;
+  if (!u || !delta || !A || !B || !C || !out) return SSM_ERR_NULL;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, workspace};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return SSM_ERR_ALIGN;
+
+  const int64_t Bsz = shape->batch, Dm = shape->dim, N = shape->dstate, L = shape->seqlen;
+  const int64_t es = shape->io_dtype == SSM_BF16 ? 2 : 4;
+  const Range ins[] = {span(u, Bsz * Dm * L, es), span(delta, Bsz * Dm * L, es), span(A, Dm * N, 4),
+                       span(B, Bsz * N * L, es), span(C, Bsz * N * L, es), span(D, D ? Dm : 0, 4),
+                       span(z, z ? Bsz * Dm * L : 0, es), span(delta_bias, delta_bias ? Dm : 0, 4),
+                       span(initial_state, initial_state ? Bsz * Dm * N : 0, 4)};
+  const Range ro = span(out, Bsz * Dm * L, es);
+  const Range rf = span(final_state, final_state ? Bsz * Dm * N : 0, 4);
+  for (size_t i = 0; i < sizeof(ins) / sizeof(ins[0]); ++i) {
+    if (overlaps(ro, ins[i])) return SSM_ERR_OVERLAP;
+    // final_state may be the very buffer initial_state points to (in-place continuation)
+    const bool same_state = (i == 8) && final_state && (const void*)final_state == (const void*)initial_state;
+    if (!same_state && overlaps(rf, ins[i])) return SSM_ERR_OVERLAP;
+  }
+  if (overlaps(ro, rf)) return SSM_ERR_OVERLAP;
+
+  const bool split = pl.S > 1 && workspace != nullptr;
+  if (pl.S > 1 && workspace != nullptr && workspace_bytes < pl.total) return SSM_ERR_WORKSPACE;
+  if (pl.S > 1 && workspace == nullptr && workspace_bytes != 0) return SSM_ERR_NULL;
+  if (split) {
+    const Range rw = span(workspace, (int64_t)pl.total, 1);
+    for (const Range& r : ins)
+      if (overlaps(rw, r)) return SSM_ERR_OVERLAP;
+    if (overlaps(rw, ro) || overlaps(rw, rf)) return SSM_ERR_OVERLAP;
+  }
+
+  ssm::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
+  p.init = initial_state; p.out = out; p.final_state = final_state;
+  p.Bsz = Bsz; p.Dm = Dm; p.N = N; p.L = L;
+  p.nblk = (int)pl.nblk;
+  p.vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;  // 8-step vector loads stay inside each row
+  p.reverse = (shape->flags & SSM_FLAG_REVERSE) ? 1 : 0;
+  p.zoh = (shape->flags & SSM_FLAG_ZOH) ? 1 : 0;
+  const bool bf16 = shape->io_dtype == SSM_BF16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  if (!split) {
+    p.S = 1;
+    p.seg_len = ((L + 63) / 64) * 64;
+    return launch_status(ssm::launch_scan(p, bf16, 0, st));
+  }
+  char* ws = static_cast<char*>(workspace);
+  p.S = (int)pl.S;
+  p.seg_len = pl.seg_len;
+  p.seg_state = reinterpret_cast<float*>(ws);
+  p.seg_dsum = reinterpret_cast<float*>(ws + pl.ws_state);
+  float* carries = reinterpret_cast<float*>(ws + pl.ws_state + pl.ws_dsum);
+  ssm_status rc = launch_status(ssm::launch_scan(p, bf16, 1, st));
+  if (rc != SSM_OK) return rc;
+  p.carries = carries;
+  rc = launch_status(ssm::launch_carry(p, st));
+  if (rc != SSM_OK) return rc;
+  return launch_status(ssm::launch_scan(p, bf16, 0, st));
+}
+
+ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t io_dtype, uint32_t flags,
+                            float* state, const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, const float* delta_bias, void* out,
+                            struct ihipStream_t* stream) {
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (flags & ~SSM_FLAG_ZOH) return SSM_ERR_UNSUPPORTED;
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 64 || batch > kMaxDim || dim > kMaxDim)
+    return SSM_ERR_SHAPE;
+  int64_t bd, bdn;
+  if (!mul_ok(batch, dim, &bd) || !mul_ok(bd, dstate, &bdn)) return SSM_ERR_SHAPE;
+  if (bd * 16 > (int64_t(1) << 31) * 256 - 1) return SSM_ERR_SHAPE;
+  if (!state || !u || !delta || !A || !B || !C || !out) return SSM_ERR_NULL;
+  const void* ptrs[] = {state, u, delta, A, B, C, D, z, delta_bias, out};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return SSM_ERR_ALIGN;
+  const int64_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const Range ins[] = {span(u, bd, es), span(delta, bd, es), span(A, dim * dstate, 4),
+                       span(B, batch * dstate, es), span(C, batch * dstate, es), span(D, D ? dim : 0, 4),
+                       span(z, z ? bd : 0, es), span(delta_bias, delta_bias ? dim : 0, 4)};
+  const Range ro = span(out, bd, es), rs = span(state, bdn, 4);
+  for (const Range& r : ins)
+    if (overlaps(ro, r) || overlaps(rs, r)) return SSM_ERR_OVERLAP;
+  if (overlaps(ro, rs)) return SSM_ERR_OVERLAP;
+
+  ssm::StepParams p;
+  memset(&p, 0, sizeof(p));
+  p.state = state; p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+  p.bias = delta_bias; p.out = out;
+  p.Bsz = batch; p.Dm = dim; p.N = dstate;
+  p.vec = (dstate % 4) == 0 ? 1 : 0;
+  p.zoh = (flags & SSM_FLAG_ZOH) ? 1 : 0;
+  return launch_status(ssm::launch_step(p, io_dtype == SSM_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// ssm_launch.h -- internal interface between the C ABI (ssm_abi.cpp) and the
+// gfx950 kernels (ssm_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* init;     // [B,D,N] state before the first step, or null (zero)
+  float* carries;        // [S,B,D,N] state entering each segment (split runs), or null
+  void* out;
+  float* final_state;
+  float* seg_state;      // [S-1,B,D,N] end state of each segment scanned from zero
+  float* seg_dsum;       // [S-1,B,D] sum of the step sizes of each segment
+  int64_t Bsz, Dm, N, L;
+  int64_t seg_len;       // steps per segment, a multiple of 64
+  int S;                 // number of segments (1: no split)
+  int nblk;              // channel blocks of 16 = ceil(Dm / 16)
+  int vec;               // rows allow 16-byte vector loads
+  int reverse;           // scan from the last step to the first
+  int zoh;               // zero-order-hold B_bar
+};
+
+struct StepParams {
+  float* state;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  void* out;
+  int64_t Bsz, Dm, N;
+  int vec;  // N % 4 == 0: state rows read and written as float4
+  int zoh;
+};
+
+hipError_t launch_scan(const ScanParams& p, bool bf16, int mode, hipStream_t s);
+hipError_t launch_carry(const ScanParams& p, hipStream_t s);
+hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports what include/ssm_scan.h
+declares, and rejects every bad argument on the host (nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_76_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+# fake, 16-byte aligned, never dereferenced addresses (validation fails before any use)
+BASE = 1 << 40
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * (1 << 32) + off)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ssm_abi_version() == L.ABI_VERSION
+
+
+def test_status_strings():
+    lib = L.load()
+    for s in range(9):
+        assert lib.ssm_status_str(s)
+    assert lib.ssm_status_str(12345) == b"unknown status"
+
+
+def scan(shape, u=None, delta=None, A=None, B=None, C=None, D=None, z=None, bias=None, h0=None,
+         out=None, fs=None, ws=None, ws_bytes=0):
+    lib = L.load()
+    args = [u, delta, A, B, C, D, z, bias, h0, out, fs]
+    return lib.ssm_scan_fwd(None if shape is None else ctypes.byref(shape), *args, ws, ws_bytes, None)
+
+
+def good_ptrs():
+    return dict(u=fake(1), delta=fake(2), A=fake(3), B=fake(4), C=fake(5), out=fake(6))
+
+
+def shp(**kw):
+    d = dict(batch=2, dim=64, dstate=16, seqlen=128, io_dtype=L.SSM_BF16, flags=0)
+    d.update(kw)
+    return L.ssm_shape(**d)
+
+
+def test_null_and_shape_errors():
+    assert scan(None) == 1
+    for name in ("u", "delta", "A", "B", "C", "out"):
+        p = good_ptrs()
+        p[name] = None
+        assert scan(shp(), **p) == 1, name
+    for bad in (dict(batch=0), dict(dim=0), dict(seqlen=0), dict(dstate=0), dict(dstate=65),
+                dict(batch=-3), dict(seqlen=1 << 41)):
+        assert scan(shp(**bad), **good_ptrs()) == 2, bad
+
+
+def test_dtype_flags_align():
+    assert scan(shp(io_dtype=2), **good_ptrs()) == 3
+    assert scan(shp(io_dtype=-1), **good_ptrs()) == 3
+    assert scan(shp(flags=4), **good_ptrs()) == 5
+    for name in ("u", "delta", "A", "B", "C", "out"):
+        p = good_ptrs()
+        p[name] = fake(list(p).index(name) + 1, off=2)
+        assert scan(shp(), **p) == 4, name
+    assert scan(shp(), D=fake(9, off=4), **good_ptrs()) == 4
+    assert scan(shp(), fs=fake(9, off=8), **good_ptrs()) == 4
+
+
+def test_overlap():
+    p = good_ptrs()
+    p["out"] = fake(1, off=16 * 5)   # inside u
+    assert scan(shp(), **p) == 8
+    p = good_ptrs()
+    assert scan(shp(), fs=fake(5, off=64), **p) == 8   # final state inside C
+    p = good_ptrs()
+    p["out"] = fake(10)
+    assert scan(shp(), fs=fake(10, off=256), **p) == 8  # final state inside out
+
+
+def test_workspace_rules():
+    lib = L.load()
+    s = shp(batch=1, dim=32, seqlen=8192)
+    need = lib.ssm_scan_workspace_size(ctypes.byref(s))
+    assert need > 0
+    assert scan(s, ws=fake(11), ws_bytes=need - 1, **good_ptrs()) == 6
+    assert scan(s, ws=None, ws_bytes=100, **good_ptrs()) == 1
+    assert lib.ssm_scan_workspace_size(ctypes.byref(shp(batch=8, dim=1536, seqlen=2048))) == 0
+    assert lib.ssm_scan_workspace_size(ctypes.byref(shp(dstate=0))) == 0
+    assert lib.ssm_scan_workspace_size(None) == 0
+
+
+def test_workspace_size_formula():
+    # split planning: shape-only; segments of >= 1024 steps (multiples of 64) for narrow problems
+    lib = L.load()
+    s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
+    S = 16                       # 64 channel blocks -> 16 segments of 65536 steps
+    bdn, bd = 1024 * 16, 1024
+    r = lambda x: (x + 255) // 256 * 256
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn)
+
+
+def step(batch=4, dim=8, dstate=16, io=L.SSM_BF16, flags=0, **kw):
+    lib = L.load()
+    p = dict(state=fake(1), u=fake(2), delta=fake(3), A=fake(4), B=fake(5), C=fake(6), D=None, z=None,
+             bias=None, out=fake(7))
+    p.update(kw)
+    return lib.ssm_state_update(batch, dim, dstate, io, flags, p["state"], p["u"], p["delta"], p["A"], p["B"],
+                                p["C"], p["D"], p["z"], p["bias"], p["out"], None)
+
+
+def test_state_update_errors():
+    assert step(io=5) == 3
+    assert step(flags=2) == 5          # reverse has no meaning for one step
+    assert step(batch=0) == 2 and step(dstate=65) == 2 and step(dim=0) == 2
+    for k in ("state", "u", "delta", "A", "B", "C", "out"):
+        assert step(**{k: None}) == 1, k
+    assert step(u=fake(2, off=2)) == 4
+    assert step(out=fake(2, off=16)) == 8    # out inside u
+    assert step(state=fake(4, off=0)) == 8   # state on top of A

@@ -1,0 +1,160 @@
+"""HIP scan and state update against the fp64 oracle (GPU).
+
+Small shapes are compared element by element (several 64-step blocks, ragged
+tails, every states-per-lane variant); the full-size workloads are run in the
+launch configuration the benchmark times and compared on sampled channels,
+which the oracle computes row by row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_76_amd import scan_fwd, state_update, workspace_size
+from selective_state_space_76_amd import workloads as W
+from tests.gpu_util import oracle_rows, rel_err, sample_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev(inp):
+    return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+
+
+def full_check(inp, h0=None, zoh=False, reverse=False, split=True, tol=None):
+    g = dev(inp)
+    out, fs = scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"), g.get("delta_bias"),
+                       None if h0 is None else h0.to(DEV), zoh=zoh, reverse=reverse, split=split)
+    torch.cuda.synchronize()
+    ref_y, ref_h = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp.get("D"), z=inp.get("z"),
+                               delta_bias=inp.get("delta_bias"), h0=h0, zoh=zoh, reverse=reverse)
+    tol = tol or tol_for(inp["u"])
+    ey, eh = rel_err(out, ref_y), rel_err(fs, ref_h)
+    print("rel_err y=%.3g state=%.3g tol=%g" % (ey, eh, tol), flush=True)
+    assert ey <= tol and eh <= tol, (ey, eh)
+    return out, fs
+
+
+def make(Bsz, Dm, N, L, dtype=torch.bfloat16, seed=0, gate=True, skip=True, bias=True, recipe="base"):
+    name = "tiny" if dtype == torch.float32 else "mamba130m"
+    w = W.WORKLOADS[name].with_shape(batch=Bsz, dim=Dm, dstate=N, seqlen=L, seed=1000 + seed, bias=bias,
+                                     recipe=recipe)
+    x = W.scan_inputs(w)
+    if not gate:
+        x["z"] = None
+    if not skip:
+        x["D"] = None
+    return x
+
+
+def test_tiny_workload_fp32():
+    print("case: tiny workload fp32 1x64x16x256", flush=True)
+    full_check(W.scan_inputs(W.WORKLOADS["tiny"]))
+
+
+@pytest.mark.parametrize("N", [16, 32, 64, 1, 5, 20, 40, 48])
+def test_states_per_lane_variants(N):
+    print("case: N=%d bf16 2x24x%dx300" % (N, N), flush=True)
+    full_check(make(2, 24, N, 300, seed=N))
+
+
+@pytest.mark.parametrize("L", [1, 7, 63, 64, 65, 129, 1000, 1001])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_ragged_lengths(L, dtype):
+    print("case: L=%d %s" % (L, dtype), flush=True)
+    full_check(make(3, 20, 16, L, dtype=dtype, seed=L))
+
+
+@pytest.mark.parametrize("opts", [dict(gate=False), dict(skip=False), dict(bias=False),
+                                  dict(gate=False, skip=False, bias=False)], ids=str)
+def test_optional_operands(opts):
+    print("case: optional operands %s" % opts, flush=True)
+    full_check(make(2, 33, 16, 257, dtype=torch.float32, seed=7, **opts))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_initial_state(dtype):
+    print("case: initial state %s" % dtype, flush=True)
+    x = make(2, 40, 16, 200, dtype=dtype, seed=3)
+    h0 = torch.randn(2, 40, 16, generator=torch.Generator().manual_seed(5))
+    full_check(x, h0=h0)
+
+
+@pytest.mark.parametrize("L", [4096, 5000, 6151])
+def test_split_path(L):
+    """Few channels, long sequence: summary + carry + output passes."""
+    print("case: split L=%d" % L, flush=True)
+    x = make(1, 40, 16, L, seed=L)
+    assert workspace_size(1, 40, 16, L) > 0
+    full_check(x)
+    h0 = torch.randn(1, 40, 16, generator=torch.Generator().manual_seed(9))
+    full_check(x, h0=h0)
+
+
+def test_split_path_fp32_wide_state():
+    print("case: split fp32 N=64", flush=True)
+    full_check(make(1, 16, 64, 3000, dtype=torch.float32, seed=11))
+
+
+@pytest.mark.parametrize("name", ["mamba130m", "mamba1p3b", "dna1m"])
+def test_full_workload_sampled(name):
+    """The full-size workload in the benchmark's launch configuration, checked on sampled channels."""
+    w = W.WORKLOADS[name]
+    print("case: full workload %s %s" % (name, (w.batch, w.dim, w.dstate, w.seqlen)), flush=True)
+    g = W.scan_inputs(w, device=DEV)
+    out, fs = scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(fs).all()
+    rows = sample_rows(w.batch, w.dim, 8 if name == "dna1m" else 48, seed=1)
+    ref_y, ref_h = oracle_rows(g, rows)
+    got_y = torch.stack([out[b, d] for b, d in rows])
+    got_h = torch.stack([fs[b, d] for b, d in rows])
+    ey, eh = rel_err(got_y, ref_y), rel_err(got_h, ref_h)
+    print("%s rel_err y=%.3g state=%.3g" % (name, ey, eh), flush=True)
+    assert ey <= 2e-2 and eh <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 64, 6])
+def test_state_update_small(dtype, N):
+    print("case: state update N=%d %s" % (N, dtype), flush=True)
+    w = W.WORKLOADS["decode2p8b"].with_shape(batch=3, dim=50, dstate=N)
+    A, Dv, bias = W.params(w)
+    state = torch.randn(3, 50, N, generator=torch.Generator().manual_seed(N))
+    st = state.to(DEV)
+    for k in range(5):
+        x = W.decode_inputs(w, k)
+        x = {kk: v.to(dtype) for kk, v in x.items()}
+        y = state_update(st, x["u"].to(DEV), x["delta"].to(DEV), A.to(DEV), x["B"].to(DEV), x["C"].to(DEV),
+                         Dv.to(DEV), x["z"].to(DEV), bias.to(DEV))
+        torch.cuda.synchronize()
+        ref_y, state = oracle.step(state, x["u"], x["delta"], A, x["B"], x["C"], D=Dv, z=x["z"], delta_bias=bias)
+        tol = 1e-4 if dtype == torch.float32 else 2e-2
+        ey, es = rel_err(y, ref_y), rel_err(st, state)
+        assert ey <= tol and es <= tol, (k, ey, es)
+
+
+def test_decode_workload_sampled():
+    """decode2p8b: 1000 consecutive tokens from a zero state; a sampled grid of batch rows x channels
+    follows the oracle's recurrence step by step."""
+    w = W.WORKLOADS["decode2p8b"]
+    print("case: decode workload %d steps" % w.steps, flush=True)
+    A, Dv, bias = W.params(w, device=DEV)
+    st = torch.zeros(w.batch, w.dim, w.dstate, device=DEV)
+    bsel = torch.tensor([0, 77, 150, w.batch - 1], device=DEV)
+    dsel = torch.tensor(sorted({0, 1, 15, 16, 17, 1023, 2500, 4096, w.dim - 1} |
+                               set(np.random.default_rng(3).integers(0, w.dim, 7).tolist())), device=DEV)
+    sub = lambda t: t.index_select(0, bsel).index_select(1, dsel).cpu()
+    ref_state = np.zeros((len(bsel), len(dsel), w.dstate))
+    A_h, D_h, bias_h = A[dsel].cpu(), Dv[dsel].cpu(), bias[dsel].cpu()
+    worst = 0.0
+    for k in range(w.steps):
+        x = W.decode_inputs(w, k, device=DEV)
+        y = state_update(st, x["u"], x["delta"], A, x["B"], x["C"], Dv, x["z"], bias)
+        ref_y, ref_state = oracle.step(ref_state, sub(x["u"]), sub(x["delta"]), A_h, x["B"][bsel].cpu(),
+                                       x["C"][bsel].cpu(), D=D_h, z=sub(x["z"]), delta_bias=bias_h)
+        if k % 100 == 99 or k == 0:
+            worst = max(worst, rel_err(sub(y), ref_y), rel_err(sub(st), ref_state))
+            print("step %d worst rel_err %.3g" % (k, worst), flush=True)
+    assert worst <= 2e-2
