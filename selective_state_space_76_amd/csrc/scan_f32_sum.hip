@@ -3,25 +3,30 @@
 
 namespace ssm {
 
-template <int NL, bool FULLN, bool ZOH, bool REV>
+template <int NL, bool ZOH, bool REV, bool VEC>
 static void go(const ScanParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((scan_kernel<float, NL, FULLN, 1, ZOH, REV>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((scan_kernel<float, NL, 1, ZOH, REV, VEC>), dim3(grid), dim3(256), 0, s, p);
 }
 
-template <int NL, bool FULLN>
+template <int NL>
 static void go_flags(const ScanParams& p, int grid, hipStream_t s) {
-  if (p.zoh) {
-    if (p.reverse) go<NL, FULLN, true, true>(p, grid, s); else go<NL, FULLN, true, false>(p, grid, s);
-  } else {
-    if (p.reverse) go<NL, FULLN, false, true>(p, grid, s); else go<NL, FULLN, false, false>(p, grid, s);
+  const int k = (p.zoh ? 4 : 0) + (p.reverse ? 2 : 0) + (p.vec ? 1 : 0);
+  switch (k) {
+    case 0: go<NL, false, false, false>(p, grid, s); break;
+    case 1: go<NL, false, false, true>(p, grid, s); break;
+    case 2: go<NL, false, true, false>(p, grid, s); break;
+    case 3: go<NL, false, true, true>(p, grid, s); break;
+    case 4: go<NL, true, false, false>(p, grid, s); break;
+    case 5: go<NL, true, false, true>(p, grid, s); break;
+    case 6: go<NL, true, true, false>(p, grid, s); break;
+    default: go<NL, true, true, true>(p, grid, s); break;
   }
 }
 
 hipError_t launch_scan_f32_sum(const ScanParams& p, int grid, hipStream_t s) {
-  const bool full = (p.N % 16) == 0;
-  if (p.N <= 16) { if (full) go_flags<1, true>(p, grid, s); else go_flags<1, false>(p, grid, s); }
-  else if (p.N <= 32) { if (full) go_flags<2, true>(p, grid, s); else go_flags<2, false>(p, grid, s); }
-  else { if (p.N == 64) go_flags<4, true>(p, grid, s); else go_flags<4, false>(p, grid, s); }
+  if (p.N <= 16) go_flags<1>(p, grid, s);
+  else if (p.N <= 32) go_flags<2>(p, grid, s);
+  else go_flags<4>(p, grid, s);
   return hipGetLastError();
 }
 

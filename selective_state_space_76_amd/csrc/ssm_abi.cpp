@@ -53,7 +53,7 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
     return false;
   int64_t bnl;
   if (!mul_ok(s->batch * s->dstate, s->seqlen, &bnl)) return false;
-  pl->nblk = (s->dim + 15) / 16;
+  pl->nblk = (s->dim + 15) / 16;  // 16 channels (4 waves) per workgroup
   const int64_t base = s->batch * pl->nblk;
   if (base > (int64_t(1) << 30)) return false;
   const int64_t L = s->seqlen;
@@ -156,7 +156,7 @@ ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta
   p.init = initial_state; p.out = out; p.final_state = final_state;
   p.Bsz = Bsz; p.Dm = Dm; p.N = N; p.L = L;
   p.nblk = (int)pl.nblk;
-  p.vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;  // 8-step vector loads stay inside each row
+  p.vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;  // 16-byte chunks stay inside each row
   p.reverse = (shape->flags & SSM_FLAG_REVERSE) ? 1 : 0;
   p.zoh = (shape->flags & SSM_FLAG_ZOH) ? 1 : 0;
   const bool bf16 = shape->io_dtype == SSM_BF16;

@@ -56,16 +56,16 @@ __device__ __forceinline__ void store_io(bf16_t* p, float v) {
   *p = __builtin_bit_cast(bf16_t, (__bf16)v);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
-// log(1 + e^x).  Above 20 the answer is x to within 2e-9 relative.  Below,
-// log1p(e) is formed as log(w) * e / (w - 1) with w = 1 + e, which cancels the
-// rounding error of w when e is small (Goldberg, "What every computer
-// scientist should know about floating-point arithmetic", theorem 4).
+// log(1 + e^x).  Above 20 the answer is x to within 2e-9 relative.  Below, with
+// e = e^x and w = fl(1 + e), log1p(e) = log(w) + log(1 + d/w) where d = e - (w - 1)
+// is the exact rounding error of w (Sterbenz); |d/w| <= 2^-24, so adding d
+// instead of log(1 + d/w) errs by under 2^-25 absolute, while it restores the
+// bits of e that w lost when e is small.
 __device__ __forceinline__ float softplus_(float x) {
   const float e = exp2_(x * kLog2e);
   const float w = 1.0f + e;
-  const float wm1 = w - 1.0f;
-  const float l = log2_(w) * kLn2;
-  const float r = (wm1 == 0.0f) ? e : l * (e * rcp_(wm1));
+  const float d = e - (w - 1.0f);
+  const float r = __builtin_fmaf(log2_(w), kLn2, d);
   return x > 20.0f ? x : r;
 }
 
@@ -87,8 +87,9 @@ template <int I, int E, typename F> __device__ __forceinline__ void static_for(F
 
 // broadcast lane J of each 16-lane row to the whole row
 template <int J> __device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0x150 + J, 0xf, 0xf, false));
+  // bound_ctrl set and full masks: every lane is written, so the move can fold
+  // into the consuming VALU op as a DPP source operand
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -106,53 +107,95 @@ __device__ __forceinline__ int xcd_remap(int i, int G) {
   return xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
 }
 
-// Load the values of 8 consecutive logical steps t..t+7 of one row into v[0..7].
-// `vec` means the row length and t are multiples of 8 (bf16) / 4 (fp32) and the
-// row is 16-byte aligned.  Steps past the row end are clamped (their values are
-// never used: dt is zero there).
-template <typename IO, bool REV>
-__device__ __forceinline__ void load8(const IO* row, int64_t t, int64_t L, bool vec, float v[8]) {
-  if (vec) {
-    const int64_t base = t < L - 8 ? t : L - 8;       // logical index of v[0]
-    const int64_t pb = REV ? (L - 8 - base) : base;   // physical start of the 8-element run
-    float w[8];
-    if constexpr (sizeof(IO) == 2) {
-      const uint4 q = *reinterpret_cast<const uint4*>(row + pb);
-      const uint32_t x[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        w[2 * k] = __uint_as_float(x[k] << 16);
-        w[2 * k + 1] = __uint_as_float(x[k] & 0xffff0000u);
-      }
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(row + pb);
-      const float4 b = *reinterpret_cast<const float4*>(row + pb + 4);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = REV ? w[7 - k] : w[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int64_t tk = t + k;
-      tk = tk < L ? tk : L - 1;
-      v[k] = to_f32(row[REV ? (L - 1 - tk) : tk]);
-    }
-  }
+// ------------------------------------------------------------- scan kernel
+
+// Lane g of each 16-lane row returns the sum over the row's lanes n of v_n[g]:
+// a reduce-scatter of a 16 x 16 tile entirely in registers.  Four butterfly
+// stages exchange half of the remaining values with partner lane g^8
+// (row_ror:8), g^7 (row_half_mirror), g^2 and g^1 (quad_perm).  In the first
+// two stages the half a lane keeps depends on lane bits 3 and 2, which are
+// exactly the DPP banks, so each output is two bank-masked DPP adds into the
+// same register; the last two stages select with v_cndmask.  Each asm block
+// starts with the two wait states a DPP read of a just-written VGPR needs.
+__device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
+  float a0, a1, a2, a3, a4, a5, a6, a7;
+  asm volatile(
+      "s_nop 1\n"
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %4, %20, %20 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %5, %21, %21 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %6, %22, %22 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %7, %23, %23 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6), "=&v"(a7)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+        "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+  float b0, b1, b2, b3;
+  asm volatile(
+      "s_nop 1\n"
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %1, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %2, %10, %10 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5), "v"(a6), "v"(a7));
+  float out, k0, s0, k1, s1, c0, c1;
+  asm volatile(
+      "v_cndmask_b32_e64 %1, %7, %9, %11\n"   // lane bit 1 set: keep b2, send b0
+      "v_cndmask_b32_e64 %2, %9, %7, %11\n"
+      "v_cndmask_b32_e64 %3, %8, %10, %11\n"  // lane bit 1 set: keep b3, send b1
+      "v_cndmask_b32_e64 %4, %10, %8, %11\n"
+      "s_nop 1\n"
+      "v_add_f32_dpp %5, %2, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "v_add_f32_dpp %6, %4, %3 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_cndmask_b32_e64 %1, %5, %6, %12\n"   // lane bit 0 set: keep c1, send c0
+      "v_cndmask_b32_e64 %2, %6, %5, %12\n"
+      "s_nop 1\n"
+      "v_add_f32_dpp %0, %2, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      : "=&v"(out), "=&v"(k0), "=&v"(s0), "=&v"(k1), "=&v"(s1), "=&v"(c0), "=&v"(c1)
+      : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "s"(0xCCCCCCCCCCCCCCCCull), "s"(0xAAAAAAAAAAAAAAAAull));
+  return out;
 }
 
-// ------------------------------------------------------------- scan kernel
-//
 // MODE 0: output pass (writes out and, for the last segment, final_state).
 // MODE 1: summary pass over segments 0..S-2 (writes seg_state and seg_dsum).
-template <typename IO, int NL, bool FULLN, int MODE, bool ZOH, bool REV>
-__global__ __launch_bounds__(256, MODE == 0 ? 3 : 2) void scan_kernel(ScanParams p) {
-  constexpr int RSTRIDE = 20;                   // floats per LDS transpose row (16 + pad, 16 B aligned)
-  constexpr int GSTRIDE = 16 * RSTRIDE + 4;     // floats per channel row
-  __shared__ float red[MODE == 0 ? 16 * GSTRIDE : 1];
+// REV: logical step t reads physical position L-1-t.  VEC: rows allow 16-byte
+// vector loads (L a multiple of 8 for bf16, of 4 for fp32, and L >= 8).
+//
+// Per 64-step block the workgroup stages, as fp32 in LDS, B (and C) for all
+// states (rows >= N stay zero) and delta/u/z of its 16 channels, all fetched
+// with coalesced 16-byte loads one block ahead into registers.
+template <typename IO, int NL, int MODE, bool ZOH, bool REV, bool VEC>
+__global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_kernel(ScanParams p) {
+  constexpr int NP = 16 * NL;                  // states padded to the lane grid
+  constexpr int TS = 68;                       // LDS tile row: 64 steps + 4 pad (floats)
+  constexpr int NT = MODE == 0 ? 2 : 1;        // staged coefficient tensors: B and C, or B only
+  constexpr int NS = MODE == 0 ? 3 : 2;        // staged channel streams: delta, u (and z)
+  constexpr int EPC = 16 / (int)sizeof(IO);    // elements per 16-byte chunk
+  constexpr int CPR = 64 / EPC;                // chunks per 64-step row
+  constexpr int NBC = NT * NP * CPR;           // coefficient chunks
+  constexpr int NCH = NBC + NS * 16 * CPR;     // + channel-stream chunks
+  constexpr int CPT = (NCH + 255) / 256;       // chunks per thread
+  __shared__ __attribute__((aligned(16))) float coef[NT * NP * TS];
+  __shared__ __attribute__((aligned(16))) float chan[NS * 16 * TS];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int r = lane >> 4, g = lane & 15;
   const int S_launch = MODE == 0 ? p.S : p.S - 1;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -161,59 +204,142 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 2) void scan_kernel(ScanParams
   const int seg = rest % S_launch;
   const int64_t b = rest / S_launch;
   const int64_t L = p.L, N = p.N, Dm = p.Dm;
-  const int64_t d = (int64_t)cb * 16 + w * 4 + r;
+  const int cl = w * 4 + r;                    // channel within the workgroup
+  const int64_t d = (int64_t)cb * 16 + cl;
   const bool dval = d < Dm;
   const int64_t dd = dval ? d : Dm - 1;
   const int64_t tb = (int64_t)seg * p.seg_len;
   const int64_t te = (tb + p.seg_len < L) ? tb + p.seg_len : L;
-  const bool vec = p.vec != 0;
+  const bool has_z = MODE == 0 && p.z != nullptr;
 
-  const IO* urow = reinterpret_cast<const IO*>(p.u) + (b * Dm + dd) * L;
-  const IO* drow = reinterpret_cast<const IO*>(p.delta) + (b * Dm + dd) * L;
-  const IO* zrow = p.z ? reinterpret_cast<const IO*>(p.z) + (b * Dm + dd) * L : nullptr;
   IO* orow = MODE == 0 ? reinterpret_cast<IO*>(p.out) + (b * Dm + dd) * L : nullptr;
   const float biasd = p.bias ? p.bias[dd] : 0.0f;
   const float Dd = p.D ? p.D[dd] : 0.0f;
 
   float Ap[NL], Aln[NL], h[NL];
-  bool nval[NL];
-  const IO* Brow[NL];
-  const IO* Crow[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int64_t n = g + 16 * i;
-    nval[i] = FULLN || n < N;
-    const int64_t nn = nval[i] ? n : N - 1;
+    const bool nv = n < N;
+    const int64_t nn = nv ? n : N - 1;
     const float a = p.A[dd * N + nn];
-    Aln[i] = nval[i] ? a : 0.0f;
+    Aln[i] = nv ? a : 0.0f;
     Ap[i] = Aln[i] * kLog2e;
     float h0 = 0.0f;
     if (MODE == 0) {
       if (p.carries) h0 = p.carries[(((int64_t)seg * p.Bsz + b) * Dm + dd) * N + nn];
       else if (p.init) h0 = p.init[(b * Dm + dd) * N + nn];
     }
-    h[i] = nval[i] ? h0 : 0.0f;
-    Brow[i] = reinterpret_cast<const IO*>(p.B) + (b * N + nn) * L;
-    Crow[i] = reinterpret_cast<const IO*>(p.C) + (b * N + nn) * L;
+    h[i] = nv ? h0 : 0.0f;
   }
-  float* rb = &red[MODE == 0 ? (w * 4 + r) * GSTRIDE : 0];
+
+  // zero the tiles once: padding states, missing channels and steps past the end read 0
+  for (int i = tid; i < NT * NP * TS; i += 256) coef[i] = 0.0f;
+  for (int i = tid; i < NS * 16 * TS; i += 256) chan[i] = 0.0f;
+
+  // ---- chunk k of this thread: source row, destination in LDS (fixed for the whole kernel)
+  const IO* src[CPT];
+  float* dst[CPT];
+  bool live[CPT];
+  int col[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = tid + 256 * k;
+    src[k] = nullptr;
+    dst[k] = coef;
+    live[k] = false;
+    col[k] = 0;
+    if (c < NBC) {
+      const int tt = c / (NP * CPR), n = (c / CPR) % NP;
+      col[k] = (c % CPR) * EPC;
+      live[k] = n < N;
+      src[k] = reinterpret_cast<const IO*>(tt == 0 ? p.B : p.C) + (b * N + (n < N ? n : 0)) * L;
+      dst[k] = coef + (tt * NP + n) * TS + col[k];
+    } else if (c < NCH) {
+      const int e = c - NBC;
+      const int st = e / (16 * CPR), row = (e / CPR) % 16;
+      col[k] = (e % CPR) * EPC;
+      const int64_t dr = (int64_t)cb * 16 + row;
+      const void* base = st == 0 ? p.delta : (st == 1 ? p.u : p.z);
+      live[k] = dr < Dm && base != nullptr;
+      src[k] = reinterpret_cast<const IO*>(live[k] ? base : p.u) + (b * Dm + (dr < Dm ? dr : 0)) * L;
+      dst[k] = chan + (st * 16 + row) * TS + col[k];
+    }
+  }
+
+  uint4 raw[CPT];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int64_t ts = t0 + col[k];  // first logical step of the chunk
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (live[k] && ts < L) {
+        if (VEC) {
+          v = *reinterpret_cast<const uint4*>(src[k] + (REV ? (L - EPC - ts) : ts));
+        } else {
+          IO e[EPC];
+#pragma unroll
+          for (int k2 = 0; k2 < EPC; ++k2) {
+            // physical order inside the chunk matches the vector path
+            const int64_t lt = REV ? (ts + EPC - 1 - k2) : (ts + k2);
+            e[k2] = (lt < L) ? src[k][REV ? (L - 1 - lt) : lt] : IO(0);
+          }
+          v = *reinterpret_cast<const uint4*>(e);
+        }
+      }
+      raw[k] = v;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if (live[k]) {
+        float f[EPC];
+        if constexpr (sizeof(IO) == 2) {
+          const uint32_t x[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) {
+            f[2 * k2] = __uint_as_float(x[k2] << 16);
+            f[2 * k2 + 1] = __uint_as_float(x[k2] & 0xffff0000u);
+          }
+        } else {
+          f[0] = __uint_as_float(raw[k].x); f[1] = __uint_as_float(raw[k].y);
+          f[2] = __uint_as_float(raw[k].z); f[3] = __uint_as_float(raw[k].w);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < EPC; k2 += 4) {
+          float4 o;
+          if (REV) o = make_float4(f[EPC - 1 - k2], f[EPC - 2 - k2], f[EPC - 3 - k2], f[EPC - 4 - k2]);
+          else o = make_float4(f[k2], f[k2 + 1], f[k2 + 2], f[k2 + 3]);
+          *reinterpret_cast<float4*>(dst[k] + k2) = o;
+        }
+      }
+    }
+  };
+
+  const float* Bt = coef;
+  const float* Ct = coef + (MODE == 0 ? NP * TS : 0);
+  const float* dch = chan + cl * TS;               // this channel's delta row
+  const float* uch = chan + (16 + cl) * TS;        // u row
+  const float* zch = chan + (32 + cl) * TS;        // z row (output pass)
   float dsum = 0.0f, dcomp = 0.0f;  // Kahan sum of dt over this lane's steps (summary pass)
 
+  fetch(tb);
   for (int64_t t0 = tb; t0 < te; t0 += 64) {
-    // ---- per (channel, step) work for the 4 steps this lane owns in the block
-    float dl[4], xu[4], uu[4], zz[4];
+    __syncthreads();  // every wave is done with the previous block's tiles
+    store();
+    if (t0 + 64 < te) fetch(t0 + 64);  // next block streams in while this one is computed
+    __syncthreads();  // tiles visible
+
+    float dl[4], xu[4], uu[4], gz[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t t = t0 + 16 * s + g;
-      const bool tv = t < te;
-      const int64_t tc = tv ? t : te - 1;
-      const int64_t tp = REV ? (L - 1 - tc) : tc;
-      const float dt = tv ? softplus_(to_f32(drow[tp]) + biasd) : 0.0f;
-      const float uv = to_f32(urow[tp]);
+      uu[s] = uch[16 * s + g];
+      gz[s] = has_z ? silu_(zch[16 * s + g]) : 1.0f;  // output gate of this step
+      const float dt = t < te ? softplus_(dch[16 * s + g] + biasd) : 0.0f;
       dl[s] = dt;
-      uu[s] = uv;
-      xu[s] = ZOH ? uv : dt * uv;
-      zz[s] = (MODE == 0 && zrow) ? to_f32(zrow[tp]) : 0.0f;
+      xu[s] = ZOH ? uu[s] : dt * uu[s];
       if (MODE == 1) {
         const float yk = dt - dcomp;
         const float tk = dsum + yk;
@@ -221,64 +347,47 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 2) void scan_kernel(ScanParams
         dsum = tk;
       }
     }
-    // ---- the recurrence, 16 steps at a time
+
+    float ys[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float pj[16];
-#pragma unroll
-      for (int jc = 0; jc < 16; jc += 8) {
-        float Bv[NL][8], Cv[NL][8];
-        const int64_t tq = t0 + 16 * s + jc;
+      // phase A: decay factors and inputs of the 16 steps
+      float av[16][NL], xv[16][NL];
+      static_for<0, 16>([&](auto j_) {
+        constexpr int j = decltype(j_)::value;
+        const float dj = row_bcast<j>(dl[s]);
+        const float xj = row_bcast<j>(xu[s]);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-          load8<IO, REV>(Brow[i], tq, L, vec, Bv[i]);
-          if (MODE == 0) load8<IO, REV>(Crow[i], tq, L, vec, Cv[i]);
-          if (!FULLN && !nval[i]) {
+          const float bv = Bt[(g + 16 * i) * TS + 16 * s + j];
+          const float a = exp2_(dj * Ap[i]);
+          av[j][i] = a;
+          if (ZOH) xv[j][i] = (dj * expm1_over_x(dj * Aln[i], a)) * (xj * bv);
+          else xv[j][i] = xj * bv;
+        }
+      });
+      // phase B: the state chain and each step's C.h terms
+      float pj[16];
+      static_for<0, 16>([&](auto j_) {
+        constexpr int j = decltype(j_)::value;
+        float acc = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) { Bv[i][k] = 0.0f; Cv[i][k] = 0.0f; }
+        for (int i = 0; i < NL; ++i) {
+          h[i] = __builtin_fmaf(av[j][i], h[i], xv[j][i]);
+          if (MODE == 0) {
+            const float cv = Ct[(g + 16 * i) * TS + 16 * s + j];
+            acc = (i == 0) ? cv * h[i] : __builtin_fmaf(cv, h[i], acc);
           }
         }
-        static_for<0, 8>([&](auto jj_) {
-          constexpr int jj = decltype(jj_)::value;
-          constexpr int j = jj;  // position within the 8-step chunk; the row lane is jc + jj
-          float dj, xj;
-          if (jc == 0) { dj = row_bcast<j>(dl[s]); xj = row_bcast<j>(xu[s]); }
-          else { dj = row_bcast<j + 8>(dl[s]); xj = row_bcast<j + 8>(xu[s]); }
-          float acc = 0.0f;
+        pj[j] = acc;
+      });
+      if (MODE == 0) ys[s] = (row_transpose_sum(pj) + Dd * uu[s]) * gz[s];
+    }
+    if (MODE == 0 && dval) {
 #pragma unroll
-          for (int i = 0; i < NL; ++i) {
-            const float a = exp2_(dj * Ap[i]);
-            float x;
-            if (ZOH) {
-              const float arg = dj * Aln[i];
-              x = (dj * expm1_over_x(arg, a)) * (xj * Bv[i][jj]);
-            } else {
-              x = xj * Bv[i][jj];
-            }
-            h[i] = __builtin_fmaf(a, h[i], x);
-            if (MODE == 0) acc = __builtin_fmaf(Cv[i][jj], h[i], acc);
-          }
-          pj[jc + jj] = acc;
-        });
-      }
-      if (MODE == 0) {
-        // ---- sum over states: row g of the [step][state] tile holds step g's terms
-#pragma unroll
-        for (int j = 0; j < 16; ++j) rb[j * RSTRIDE + g] = pj[j];
-        wave_sync();
-        const float4 q0 = *reinterpret_cast<const float4*>(rb + g * RSTRIDE + 0);
-        const float4 q1 = *reinterpret_cast<const float4*>(rb + g * RSTRIDE + 4);
-        const float4 q2 = *reinterpret_cast<const float4*>(rb + g * RSTRIDE + 8);
-        const float4 q3 = *reinterpret_cast<const float4*>(rb + g * RSTRIDE + 12);
-        wave_sync();
-        const float y0 = ((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w));
-        const float y1 = ((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w));
+      for (int s = 0; s < 4; ++s) {
         const int64_t t = t0 + 16 * s + g;
-        if (dval && t < te) {
-          float y = (y0 + y1) + Dd * uu[s];
-          if (zrow) y *= silu_(zz[s]);
-          store_io(orow + (REV ? (L - 1 - t) : t), y);
-        }
+        if (t < te) store_io(orow + (REV ? (L - 1 - t) : t), ys[s]);
       }
     }
   }
@@ -287,7 +396,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 2) void scan_kernel(ScanParams
     if (p.final_state && seg == p.S - 1 && dval) {
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if (nval[i]) p.final_state[(b * Dm + d) * N + g + 16 * i] = h[i];
+        if (g + 16 * i < N) p.final_state[(b * Dm + d) * N + g + 16 * i] = h[i];
     }
   } else {
     // row sum of the lanes' step-size sums
@@ -298,7 +407,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 2) void scan_kernel(ScanParams
     if (dval) {
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if (nval[i]) p.seg_state[((int64_t)seg * p.Bsz * Dm) * N + bd * N + g + 16 * i] = h[i];
+        if (g + 16 * i < N) p.seg_state[((int64_t)seg * p.Bsz * Dm) * N + bd * N + g + 16 * i] = h[i];
       if (g == 0) p.seg_dsum[(int64_t)seg * p.Bsz * Dm + bd] = ds;
     }
   }

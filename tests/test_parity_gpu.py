@@ -158,3 +158,46 @@ def test_decode_workload_sampled():
             worst = max(worst, rel_err(sub(y), ref_y), rel_err(sub(st), ref_state))
             print("step %d worst rel_err %.3g" % (k, worst), flush=True)
     assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("L", [300, 1000, 1001, 4500])
+def test_zoh(dtype, L):
+    """Exact zero-order-hold B_bar (the oracle's ZOH is pinned to scipy's cont2discrete)."""
+    print("case: zoh L=%d %s" % (L, dtype), flush=True)
+    x = make(1 if L > 4000 else 2, 40 if L > 4000 else 24, 16, L, dtype=dtype, seed=L + 1)
+    full_check(x, zoh=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("L", [300, 1000, 1001, 4500])
+def test_reverse(dtype, L):
+    """Backward-in-time scan, with and without a sequence split and an initial state."""
+    print("case: reverse L=%d %s" % (L, dtype), flush=True)
+    x = make(1 if L > 4000 else 2, 40 if L > 4000 else 24, 16, L, dtype=dtype, seed=L + 2)
+    full_check(x, reverse=True)
+    h0 = torch.randn(x["u"].shape[0], x["u"].shape[1], 16, generator=torch.Generator().manual_seed(L))
+    full_check(x, h0=h0, reverse=True)
+
+
+def test_reverse_zoh_wide_state():
+    print("case: reverse+zoh N=64", flush=True)
+    full_check(make(2, 20, 64, 700, dtype=torch.float32, seed=99), zoh=True, reverse=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_state_update_zoh(dtype):
+    print("case: state update zoh %s" % dtype, flush=True)
+    w = W.WORKLOADS["decode2p8b"].with_shape(batch=3, dim=40, dstate=16)
+    A, Dv, bias = W.params(w)
+    state = torch.randn(3, 40, 16, generator=torch.Generator().manual_seed(4))
+    st = state.to(DEV)
+    for k in range(4):
+        x = {kk: v.to(dtype) for kk, v in W.decode_inputs(w, k).items()}
+        y = state_update(st, x["u"].to(DEV), x["delta"].to(DEV), A.to(DEV), x["B"].to(DEV), x["C"].to(DEV),
+                         Dv.to(DEV), x["z"].to(DEV), bias.to(DEV), zoh=True)
+        torch.cuda.synchronize()
+        ref_y, state = oracle.step(state, x["u"], x["delta"], A, x["B"], x["C"], D=Dv, z=x["z"], delta_bias=bias,
+                                   zoh=True)
+        tol = 1e-4 if dtype == torch.float32 else 2e-2
+        assert rel_err(y, ref_y) <= tol and rel_err(st, state) <= tol
