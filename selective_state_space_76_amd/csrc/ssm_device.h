@@ -191,8 +191,9 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
   constexpr int NBC = NT * NP * CPR;           // coefficient chunks
   constexpr int NCH = NBC + NS * 16 * CPR;     // + channel-stream chunks
   constexpr int CPT = (NCH + 255) / 256;       // chunks per thread
-  __shared__ __attribute__((aligned(16))) float coef[NT * NP * TS];
-  __shared__ __attribute__((aligned(16))) float chan[NS * 16 * TS];
+  constexpr int NBUF = NL == 1 ? 2 : 1;        // double-buffered tiles when LDS allows (one barrier per block)
+  constexpr int TILE = NT * NP * TS + NS * 16 * TS;
+  __shared__ __attribute__((aligned(16))) float tiles[NBUF * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -234,19 +235,18 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
   }
 
   // zero the tiles once: padding states, missing channels and steps past the end read 0
-  for (int i = tid; i < NT * NP * TS; i += 256) coef[i] = 0.0f;
-  for (int i = tid; i < NS * 16 * TS; i += 256) chan[i] = 0.0f;
+  for (int i = tid; i < NBUF * TILE; i += 256) tiles[i] = 0.0f;
 
-  // ---- chunk k of this thread: source row, destination in LDS (fixed for the whole kernel)
+  // ---- chunk k of this thread: source row, destination offset in a tile (fixed for the whole kernel)
   const IO* src[CPT];
-  float* dst[CPT];
+  int dst[CPT];
   bool live[CPT];
   int col[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     const int c = tid + 256 * k;
     src[k] = nullptr;
-    dst[k] = coef;
+    dst[k] = 0;
     live[k] = false;
     col[k] = 0;
     if (c < NBC) {
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
       col[k] = (c % CPR) * EPC;
       live[k] = n < N;
       src[k] = reinterpret_cast<const IO*>(tt == 0 ? p.B : p.C) + (b * N + (n < N ? n : 0)) * L;
-      dst[k] = coef + (tt * NP + n) * TS + col[k];
+      dst[k] = (tt * NP + n) * TS + col[k];
     } else if (c < NCH) {
       const int e = c - NBC;
       const int st = e / (16 * CPR), row = (e / CPR) % 16;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
       const void* base = st == 0 ? p.delta : (st == 1 ? p.u : p.z);
       live[k] = dr < Dm && base != nullptr;
       src[k] = reinterpret_cast<const IO*>(live[k] ? base : p.u) + (b * Dm + (dr < Dm ? dr : 0)) * L;
-      dst[k] = chan + (st * 16 + row) * TS + col[k];
+      dst[k] = NT * NP * TS + (st * 16 + row) * TS + col[k];
     }
   }
 
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
       raw[k] = v;
     }
   };
-  auto store = [&]() {
+  auto store = [&](float* tile) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       if (live[k]) {
@@ -311,33 +311,55 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
           float4 o;
           if (REV) o = make_float4(f[EPC - 1 - k2], f[EPC - 2 - k2], f[EPC - 3 - k2], f[EPC - 4 - k2]);
           else o = make_float4(f[k2], f[k2 + 1], f[k2 + 2], f[k2 + 3]);
-          *reinterpret_cast<float4*>(dst[k] + k2) = o;
+          *reinterpret_cast<float4*>(tile + dst[k] + k2) = o;
         }
       }
     }
   };
 
-  const float* Bt = coef;
-  const float* Ct = coef + (MODE == 0 ? NP * TS : 0);
-  const float* dch = chan + cl * TS;               // this channel's delta row
-  const float* uch = chan + (16 + cl) * TS;        // u row
-  const float* zch = chan + (32 + cl) * TS;        // z row (output pass)
   float dsum = 0.0f, dcomp = 0.0f;  // Kahan sum of dt over this lane's steps (summary pass)
 
   fetch(tb);
-  for (int64_t t0 = tb; t0 < te; t0 += 64) {
-    __syncthreads();  // every wave is done with the previous block's tiles
-    store();
-    if (t0 + 64 < te) fetch(t0 + 64);  // next block streams in while this one is computed
-    __syncthreads();  // tiles visible
+  if (NBUF == 2) {  // block 0 goes straight into buffer 0; block 1 streams in during block 0
+    store(tiles);
+    fetch(tb + 64);
+  }
+  int64_t blk = 0;
+  for (int64_t t0 = tb; t0 < te; t0 += 64, ++blk) {
+    float* tile = tiles + (NBUF == 2 ? (int)(blk & 1) * TILE : 0);
+    if (NBUF == 2) {
+      // buffer blk&1 holds this block (written during the previous one); the other buffer's last
+      // readers finished the previous block before this barrier, so the next block can go there
+      __syncthreads();
+      if (t0 + 64 < te) {
+        store(tiles + (int)((blk + 1) & 1) * TILE);
+        if (t0 + 128 < te) fetch(t0 + 128);
+      }
+    } else {
+      __syncthreads();  // every wave is done with the previous block's tile
+      store(tile);
+      if (t0 + 64 < te) fetch(t0 + 64);  // next block streams in while this one is computed
+      __syncthreads();  // tile visible
+    }
+    const float* Bt = tile;
+    const float* Ct = tile + (MODE == 0 ? NP * TS : 0);
+    const float* dch = tile + NT * NP * TS + cl * TS;          // this channel's delta row
+    const float* uch = tile + NT * NP * TS + (16 + cl) * TS;   // u row
+    const float* zch = tile + NT * NP * TS + (32 + cl) * TS;   // z row (output pass)
 
-    float dl[4], xu[4], uu[4], gz[4];
+    // this lane's own steps: issue all LDS reads first, then compute
+    float dl[4], xu[4], uu[4], gz[4], zr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      dl[s] = dch[16 * s + g];
+      uu[s] = uch[16 * s + g];
+      zr[s] = has_z ? zch[16 * s + g] : 0.0f;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t t = t0 + 16 * s + g;
-      uu[s] = uch[16 * s + g];
-      gz[s] = has_z ? silu_(zch[16 * s + g]) : 1.0f;  // output gate of this step
-      const float dt = t < te ? softplus_(dch[16 * s + g] + biasd) : 0.0f;
+      gz[s] = has_z ? silu_(zr[s]) : 1.0f;  // output gate of this step
+      const float dt = t < te ? softplus_(dl[s] + biasd) : 0.0f;
       dl[s] = dt;
       xu[s] = ZOH ? uu[s] : dt * uu[s];
       if (MODE == 1) {
@@ -348,9 +370,33 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
       }
     }
 
+    // B and C of a sub-block in registers; with one state per lane the next
+    // sub-block's values are read from LDS while this one computes
+    constexpr bool PREF = NL == 1;
+    float bcur[NL][16], ccur[NL][16], bnxt[NL][16], cnxt[NL][16];
+    auto read_bc = [&](int s, float (&bb)[NL][16], float (&cc)[NL][16]) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 vb = *reinterpret_cast<const float4*>(Bt + (g + 16 * i) * TS + 16 * s + 4 * q);
+          bb[i][4 * q] = vb.x; bb[i][4 * q + 1] = vb.y; bb[i][4 * q + 2] = vb.z; bb[i][4 * q + 3] = vb.w;
+          if (MODE == 0) {
+            const float4 vc = *reinterpret_cast<const float4*>(Ct + (g + 16 * i) * TS + 16 * s + 4 * q);
+            cc[i][4 * q] = vc.x; cc[i][4 * q + 1] = vc.y; cc[i][4 * q + 2] = vc.z; cc[i][4 * q + 3] = vc.w;
+          }
+        }
+    };
+    if (PREF) read_bc(0, bcur, ccur);
+
     float ys[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (PREF) {
+        if (s + 1 < 4) read_bc(s + 1, bnxt, cnxt);
+      } else {
+        read_bc(s, bcur, ccur);
+      }
       // phase A: decay factors and inputs of the 16 steps
       float av[16][NL], xv[16][NL];
       static_for<0, 16>([&](auto j_) {
@@ -359,7 +405,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
         const float xj = row_bcast<j>(xu[s]);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-          const float bv = Bt[(g + 16 * i) * TS + 16 * s + j];
+          const float bv = bcur[i][j];
           const float a = exp2_(dj * Ap[i]);
           av[j][i] = a;
           if (ZOH) xv[j][i] = (dj * expm1_over_x(dj * Aln[i], a)) * (xj * bv);
@@ -375,13 +421,19 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
         for (int i = 0; i < NL; ++i) {
           h[i] = __builtin_fmaf(av[j][i], h[i], xv[j][i]);
           if (MODE == 0) {
-            const float cv = Ct[(g + 16 * i) * TS + 16 * s + j];
+            const float cv = ccur[i][j];
             acc = (i == 0) ? cv * h[i] : __builtin_fmaf(cv, h[i], acc);
           }
         }
         pj[j] = acc;
       });
       if (MODE == 0) ys[s] = (row_transpose_sum(pj) + Dd * uu[s]) * gz[s];
+      if (PREF && s + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) { bcur[i][j] = bnxt[i][j]; ccur[i][j] = cnxt[i][j]; }
+      }
     }
     if (MODE == 0 && dval) {
 #pragma unroll
