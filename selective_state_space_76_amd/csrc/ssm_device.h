@@ -39,6 +39,7 @@
 namespace ssm {
 
 typedef uint16_t bf16_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -490,12 +491,25 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   float* st = p.state + cc * N + n0;
   const bool vec4 = p.vec != 0 && n0 < N;  // N % 4 == 0: whole quads
   if (vec4) {
-    const float4 hq = *reinterpret_cast<const float4*>(st);
+    // the state is streamed once per step: nontemporal accesses keep it from displacing
+    // the reused operands (A, B, C) in the caches
+    const f32x4 hq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st));
     const float4 aq = *reinterpret_cast<const float4*>(p.A + d * N + n0);
     hv[0] = hq.x; hv[1] = hq.y; hv[2] = hq.z; hv[3] = hq.w;
     Av[0] = aq.x; Av[1] = aq.y; Av[2] = aq.z; Av[3] = aq.w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { Bv[k] = to_f32(Bp[n0 + k]); Cv[k] = to_f32(Cp[n0 + k]); }
+    if constexpr (sizeof(IO) == 2) {  // 4 bf16 states = one 8-byte load each
+      const uint2 bq = *reinterpret_cast<const uint2*>(Bp + n0);
+      const uint2 cq = *reinterpret_cast<const uint2*>(Cp + n0);
+      Bv[0] = __uint_as_float(bq.x << 16); Bv[1] = __uint_as_float(bq.x & 0xffff0000u);
+      Bv[2] = __uint_as_float(bq.y << 16); Bv[3] = __uint_as_float(bq.y & 0xffff0000u);
+      Cv[0] = __uint_as_float(cq.x << 16); Cv[1] = __uint_as_float(cq.x & 0xffff0000u);
+      Cv[2] = __uint_as_float(cq.y << 16); Cv[3] = __uint_as_float(cq.y & 0xffff0000u);
+    } else {
+      const float4 bq = *reinterpret_cast<const float4*>(Bp + n0);
+      const float4 cq = *reinterpret_cast<const float4*>(Cp + n0);
+      Bv[0] = bq.x; Bv[1] = bq.y; Bv[2] = bq.z; Bv[3] = bq.w;
+      Cv[0] = cq.x; Cv[1] = cq.y; Cv[2] = cq.z; Cv[3] = cq.w;
+    }
   } else if (p.vec == 0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -526,7 +540,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   }
   if (cval) {
     if (vec4) {
-      *reinterpret_cast<float4*>(st) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+      const f32x4 o = {hv[0], hv[1], hv[2], hv[3]};
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(st));
     } else if (p.vec == 0) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
