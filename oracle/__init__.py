@@ -15,7 +15,10 @@ What it computes follows the pages' definition of the selective SSM:
     section);
   * optional exact ZOH B_bar (freeguideonline tutorial, section 2.2), reverse
     direction (fsdata.site article, section 7 pitfalls table) and a given
-    initial state (mlqm.cn article, section 6.2, chunked long sequences).
+    initial state (mlqm.cn article, section 6.2, chunked long sequences);
+  * the step that produces u: causal depthwise conv1d of width K with a bias,
+    cut to the sequence length, then SiLU (ai.xwebgame.com Mamba page, the
+    PyTorch block's step 2).
 """
 from __future__ import annotations
 
@@ -54,6 +57,8 @@ class Oracle:
         lib.oracle_scan_f64.restype = ctypes.c_int
         lib.oracle_step_f64.argtypes = [i64, i64, i64, d] + [d] * 8 + [d, ctypes.c_int, ctypes.c_int]
         lib.oracle_step_f64.restype = ctypes.c_int
+        lib.oracle_conv1d_f64.argtypes = [i64, i64, i64, i64] + [d] * 6 + [ctypes.c_int]
+        lib.oracle_conv1d_f64.restype = ctypes.c_int
         self.lib = lib
 
     def scan(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
@@ -99,6 +104,33 @@ class Oracle:
             raise RuntimeError("oracle_step_f64 failed (%d)" % rc)
         return out, st
 
+    def conv1d(self, x, w, bias=None, state=None, threads=0):
+        """Causal depthwise conv1d + bias + SiLU in fp64.
+
+        x: [Bsz, Dm, L]; w: [Dm, K]; bias: [Dm] or None; state: [Bsz, Dm, K-1] inputs before
+        x (oldest first) or None (zeros).  Returns (u [Bsz,Dm,L], state_out [Bsz,Dm,K-1]).
+        """
+        x, w, bias, state = map(_f64, (x, w, bias, state))
+        Bsz, Dm, L = x.shape
+        K = w.shape[1]
+        assert w.shape == (Dm, K) and K >= 1
+        assert bias is None or bias.shape == (Dm,)
+        assert state is None or state.shape == (Bsz, Dm, K - 1)
+        u = np.empty((Bsz, Dm, L), np.float64)
+        so = np.empty((Bsz, Dm, K - 1), np.float64)
+        rc = self.lib.oracle_conv1d_f64(Bsz, Dm, L, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(state),
+                                        _ptr(u), _ptr(so), int(threads))
+        if rc != 0:
+            raise RuntimeError("oracle_conv1d_f64 failed (%d)" % rc)
+        return u, so
+
+    def conv_step(self, state, x, w, bias=None):
+        """One decode step of the conv: the L = 1 case.  x: [Bsz, Dm]; state: [Bsz, Dm, K-1].
+        Returns (u [Bsz, Dm], new_state [Bsz, Dm, K-1])."""
+        x = _f64(x)
+        u, so = self.conv1d(x[:, :, None], w, bias, state)
+        return u[:, :, 0], so
+
 
 def compile_variant(src_text: str, out_path: str) -> str:
     """Build an edited copy of the oracle source (used to check that the pins catch mistakes)."""
@@ -138,6 +170,14 @@ def scan(*args, **kw):
 
 def step(*args, **kw):
     return default().step(*args, **kw)
+
+
+def conv1d(*args, **kw):
+    return default().conv1d(*args, **kw)
+
+
+def conv_step(*args, **kw):
+    return default().conv_step(*args, **kw)
 
 
 def _f64(x):

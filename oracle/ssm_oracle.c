@@ -36,6 +36,12 @@
  * Layouts (row-major, contiguous):
  *   u, delta, z, out : [Bsz, Dm, L]     B, C : [Bsz, N, L]
  *   A : [Dm, N]   D, bias : [Dm]   h0, final_state : [Bsz, Dm, N]
+ *
+ * The step that produces u (oracle_conv1d_f64) follows the block of [xw-code]:
+ * a depthwise 1-D convolution of width K over time with K-1 zeros of padding
+ * on the left, its output cut to the first L steps (so step t only sees steps
+ * t-K+1 .. t), a per-channel bias, then SiLU.  Like the page's nn.Conv1d it
+ * is a cross-correlation: weight tap k multiplies the input K-1-k steps back.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,7 +60,7 @@ static double softplus_f64(double x) {
 
 static double silu_f64(double z) { return z / (1.0 + exp(-z)); }
 
-int oracle_abi_version(void) { return 2; }
+int oracle_abi_version(void) { return 3; }
 
 /* Threads an OpenMP region of the oracle uses by default (1 without OpenMP). */
 int oracle_max_threads(void) {
@@ -155,4 +161,44 @@ int oracle_step_f64(int64_t Bsz, int64_t Dm, int64_t N, double* state,
     out[r] = y;
   }
   return 0;
+}
+
+/* Causal depthwise convolution + bias + SiLU (the block's step 2 in [xw-code]).
+ *   x, u            : [Bsz, Dm, L]
+ *   w               : [Dm, K]    tap k weighs input step t - (K-1) + k
+ *   bias            : [Dm] or NULL (zero)
+ *   state_in        : [Bsz, Dm, K-1] or NULL (zeros): the K-1 inputs before x,
+ *                     oldest first, so a sequence can be processed in pieces
+ *   state_out       : [Bsz, Dm, K-1] or NULL: the last K-1 inputs of the
+ *                     sequence state_in followed by x, oldest first
+ *   u[t] = silu(bias + sum_k w[k] * xe[t + k]), xe = state_in followed by x. */
+int oracle_conv1d_f64(int64_t Bsz, int64_t Dm, int64_t L, int64_t K,
+                      const double* x, const double* w, const double* bias,
+                      const double* state_in, double* u, double* state_out,
+                      int nthreads) {
+  if (Bsz < 0 || Dm < 0 || L < 0 || K < 1 || !x || !w || !u) return -1;
+  const int64_t rows = Bsz * Dm, H = K - 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int bad = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t d = r % Dm;
+    double* xe = (double*)malloc((size_t)(H + L + 1) * sizeof(double));
+    if (!xe) { bad = 1; continue; }
+    for (int64_t j = 0; j < H; ++j) xe[j] = state_in ? state_in[r * H + j] : 0.0;
+    for (int64_t t = 0; t < L; ++t) xe[H + t] = x[r * L + t];
+    for (int64_t t = 0; t < L; ++t) {
+      double v = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < K; ++k) v += w[d * K + k] * xe[t + k];
+      u[r * L + t] = silu_f64(v);
+    }
+    if (state_out)
+      for (int64_t j = 0; j < H; ++j) state_out[r * H + j] = xe[L + j];
+    free(xe);
+  }
+  return bad ? -1 : 0;
 }

@@ -306,7 +306,104 @@ def check_permutation_equivariance(orc):
     assert np.array_equal(yp, y[pb][:, pd]) and np.array_equal(hp, h[pb][:, pd])
 
 
+# ---- the conv step that produces u (ai.xwebgame.com Mamba page, PyTorch block step 2) ----
+
+def conv_inputs(seed, Bsz=2, Dm=3, L=37, K=4, bias=True, state=False):
+    rng = np.random.default_rng(seed)
+    inp = dict(x=rng.standard_normal((Bsz, Dm, L)), w=rng.standard_normal((Dm, K)),
+               bias=rng.standard_normal(Dm) if bias else None)
+    if state:
+        inp["state"] = rng.standard_normal((Bsz, Dm, K - 1))
+    return inp
+
+
+def _torch_block_conv(x, w, bias, state=None):
+    """The page's formulation with torch's own conv: a depthwise nn.Conv1d-style call with
+    K-1 padding on both sides, output cut to the first L steps, then SiLU.  With a state
+    the state is prepended and no padding is used."""
+    import torch
+    import torch.nn.functional as F
+    xt = torch.from_numpy(np.ascontiguousarray(x))
+    wt = torch.from_numpy(np.ascontiguousarray(w))[:, None, :]
+    bt = None if bias is None else torch.from_numpy(np.ascontiguousarray(bias))
+    Dm, K = w.shape
+    L = x.shape[-1]
+    if state is None:
+        v = F.conv1d(xt, wt, bt, padding=K - 1, groups=Dm)[..., :L]
+    else:
+        v = F.conv1d(torch.cat([torch.from_numpy(state), xt], dim=-1), wt, bt, groups=Dm)
+    return v.numpy() * scipy.special.expit(v.numpy())
+
+
+def check_conv_library(orc):
+    for K in (1, 2, 3, 4):
+        for st in (False, True):
+            for bias in (True, False):
+                inp = conv_inputs(120 + K, K=K, state=st, bias=bias)
+                u, _ = orc.conv1d(**inp)
+                assert rel(u, _torch_block_conv(**inp)) < 1e-13, (K, st, bias)
+
+
+def check_conv_impulse(orc):
+    """A unit impulse at t0 yields pre-activations w[K-1-j] at t0 + j and 0 elsewhere."""
+    Dm, K, L, t0 = 2, 4, 12, 5
+    w = np.array([[0.5, -1.25, 2.0, 0.75], [-0.3, 0.9, 1.7, -2.2]])
+    x = np.zeros((1, Dm, L))
+    x[..., t0] = 1.0
+    u, _ = orc.conv1d(x, w)
+    v = np.zeros((Dm, L))
+    for j in range(K):
+        v[:, t0 + j] = w[:, K - 1 - j]
+    assert rel(u[0], _silu(v)) < 1e-15
+
+
+def check_conv_k1(orc):
+    inp = conv_inputs(131, K=1)
+    u, so = orc.conv1d(**inp)
+    v = inp["w"][None, :, 0:1] * inp["x"] + inp["bias"][None, :, None]
+    assert rel(u, _silu(v)) < 1e-15 and so.shape == (2, 3, 0)
+
+
+def check_conv_state_out(orc):
+    K = 4
+    for L in (1, 2, 3, 4, 9):
+        inp = conv_inputs(140 + L, L=L, K=K, state=True)
+        _, so = orc.conv1d(**inp)
+        ext = np.concatenate([inp["state"], inp["x"]], axis=-1)
+        assert np.array_equal(so, ext[..., -(K - 1):]), L
+
+
+def check_conv_chunking(orc):
+    """Processing in pieces with the state carried equals one pass; so does the per-step form."""
+    inp = conv_inputs(151, L=23)
+    u, so = orc.conv1d(**inp)
+    for cut in (1, 2, 3, 10, 22):
+        u1, s1 = orc.conv1d(inp["x"][..., :cut], inp["w"], inp["bias"])
+        u2, s2 = orc.conv1d(inp["x"][..., cut:], inp["w"], inp["bias"], s1)
+        assert rel(np.concatenate([u1, u2], axis=-1), u) < 1e-15 and np.array_equal(s2, so)
+    st = np.zeros((2, 3, 3))
+    for t in range(23):
+        ut, st = orc.conv_step(st, inp["x"][..., t], inp["w"], inp["bias"])
+        assert rel(ut, u[..., t]) < 1e-15
+    assert np.array_equal(st, so)
+
+
+def check_conv_causality(orc):
+    inp = conv_inputs(161, L=20)
+    u, _ = orc.conv1d(**inp)
+    for s in (0, 9, 19):
+        x2 = inp["x"].copy()
+        x2[..., s] += 2.0
+        u2, _ = orc.conv1d(x2, inp["w"], inp["bias"])
+        assert np.array_equal(u2[..., :s], u[..., :s])
+        assert not np.allclose(u2[..., s], u[..., s])
+        if s + 4 < 20:
+            assert np.array_equal(u2[..., s + 4:], u[..., s + 4:])   # width 4: no reach beyond
+
+
 ALL_CHECKS = [check_brute_force, check_initial_state, check_lti_closed_form, check_zoh_library,
               check_a_zero_cumsum, check_small_step_skip, check_single_step_closed_form,
               check_step_matches_scan, check_softplus_silu, check_linearity_in_u, check_causality,
-              check_reverse, check_permutation_equivariance]
+              check_reverse, check_permutation_equivariance,
+              check_conv_library, check_conv_impulse, check_conv_k1, check_conv_state_out,
+              check_conv_chunking, check_conv_causality]

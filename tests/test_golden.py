@@ -50,3 +50,17 @@ def test_hand_worked(orc, case):
         zoh=case["zoh"], reverse=case["reverse"])
     np.testing.assert_allclose(y[0, 0], [ev(v) for v in case["y"]], rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(h[0, 0], [ev(v) for v in case["final_state"]], rtol=1e-14, atol=1e-15)
+
+
+with open(os.path.join(HERE, "golden", "conv_hand_worked.json")) as f:
+    CONV_GOLD = json.load(f)
+
+
+@pytest.mark.parametrize("case", CONV_GOLD["cases"], ids=[c["name"] for c in CONV_GOLD["cases"]])
+def test_conv_hand_worked(orc, case):
+    K = case["K"]
+    x = np.array([ev(v) for v in case["x"]]).reshape(1, 1, -1)
+    st = None if case["state"] is None else np.array(case["state"], float).reshape(1, 1, K - 1)
+    u, so = orc.conv1d(x, np.array(case["w"], float).reshape(1, K), np.array([ev(case["bias"])]), st)
+    np.testing.assert_allclose(u[0, 0], [ev(v) for v in case["u"]], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(so[0, 0], [ev(v) for v in case["state_out"]], rtol=1e-14, atol=1e-15)

@@ -35,6 +35,17 @@ MUTANTS = [
      "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n] * 0.5;"),
     ("step_bias_dropped", "const double dt = softplus_f64(delta[r] + (bias ? bias[d] : 0.0));",
      "const double dt = softplus_f64(delta[r]);"),
+    ("conv_taps_flipped", "v += w[d * K + k] * xe[t + k];", "v += w[d * K + (K - 1 - k)] * xe[t + k];"),
+    ("conv_lookahead", "v += w[d * K + k] * xe[t + k];",
+     "v += w[d * K + k] * xe[t + k + 1 < H + L ? t + k + 1 : t + k];"),
+    ("conv_bias_dropped", "double v = bias ? bias[d] : 0.0;", "double v = 0.0;"),
+    ("conv_no_silu", "u[r * L + t] = silu_f64(v);", "u[r * L + t] = v;"),
+    ("conv_state_ignored", "xe[j] = state_in ? state_in[r * H + j] : 0.0;", "xe[j] = 0.0;"),
+    ("conv_state_reversed", "xe[j] = state_in ? state_in[r * H + j] : 0.0;",
+     "xe[j] = state_in ? state_in[r * H + (H - 1 - j)] : 0.0;"),
+    ("conv_state_out_shifted", "state_out[r * H + j] = xe[L + j];",
+     "state_out[r * H + j] = xe[L + j > 0 ? L + j - 1 : 0];"),
+    ("conv_weight_row_stride", "v += w[d * K + k] * xe[t + k];", "v += w[k * Dm + d] * xe[t + k];"),
 ]
 
 
