@@ -8,7 +8,9 @@ scan, carry, output epilogue: the entire prefill/training-forward path) with
 every input already resident in HBM.  The timed loop rotates through enough
 independent input sets that they cannot be served from the 256 MB Infinity
 Cache.  The same JSON line also carries the decode path (ssm_state_update) on
-the 2.8B-shaped generation workload and the fp64 CPU oracle's rate on the host.
+the 2.8B-shaped generation workload, the conv + SiLU step that produces u
+(ssm_conv1d_fwd on the same [B, D, L] shape, ssm_conv1d_update on the decode
+shape) and the fp64 CPU oracle's rate on the host.
 
 Progress goes to stderr; stdout gets exactly one JSON line.
 """
@@ -158,6 +160,102 @@ def bench_decode(args, torch, ssm, W):
     }
 
 
+def conv_bytes(w, K) -> int:
+    """Algorithmic HBM bytes of one conv prefill call: x read, u written, the carried-out state
+    written, weights and bias read."""
+    s = 4 if w.io == "f32" else 2
+    BDL, BD = w.batch * w.dim * w.seqlen, w.batch * w.dim
+    return 2 * s * BDL + s * BD * (K - 1) + 4 * w.dim * (K + 1)
+
+
+def conv_step_bytes(w, K) -> int:
+    """Algorithmic HBM bytes of one conv decode step: state read + written, x read, u written,
+    weights and bias read."""
+    s = 4 if w.io == "f32" else 2
+    BD = w.batch * w.dim
+    return 2 * s * BD * (K - 1) + 2 * s * BD + 4 * w.dim * (K + 1)
+
+
+def bench_conv(args, torch, ssm, W, K=4):
+    """The conv + SiLU step that produces u, on the scan workload's [B, D, L] shape, and its
+    decode form on the generation workload; events bracket each launch on the launch stream."""
+    w = W.WORKLOADS[args.workload]
+    per_set = conv_bytes(w, K)
+    R = max(1, min(8, math.ceil(2 * MALL_BYTES / per_set)))
+    sets = []
+    for k in range(R):
+        c = W.conv_inputs(w.with_shape(seed=w.seed + 1000 * k), K, device="cuda")
+        c["u"] = torch.empty_like(c["x"])
+        c["so"] = torch.empty((w.batch, w.dim, K - 1), dtype=c["x"].dtype, device="cuda")
+        sets.append(c)
+    for k in range(args.warmup):
+        c = sets[k % R]
+        ssm.conv1d_fwd(c["x"], c["weight"], c["bias"], out=c["u"], final_state=c["so"])
+    n = max(args.steps, 20)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        c = sets[k % R]
+        ev[2 * k].record()
+        ssm.conv1d_fwd(c["x"], c["weight"], c["bias"], out=c["u"], final_state=c["so"])
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n))
+    mean = sum(ms) / n
+    b = conv_bytes(w, K)
+    pre = {"workload": "%s shape (%d x %d x %d), width %d, %s" % (w.name, w.batch, w.dim, w.seqlen, K, w.io),
+           "rotated_input_sets": R, "launch_ms": mean, "launch_ms_median": ms[n // 2],
+           "roofline": {"bound": "hbm", "achieved": b / (mean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "traffic": traffic_from_profile("conv_" + w.name, 1), "algorithmic_bytes_per_launch": b}}
+
+    wd = W.WORKLOADS["decode2p8b"]
+    steps = min(args.decode_steps, 200)
+    wt, bias = W.conv_params(wd, K, device="cuda")
+    per_state = 2 * wd.batch * wd.dim * (K - 1)
+    nstate = max(1, math.ceil(1.25 * MALL_BYTES / per_state))
+    states = [torch.zeros((wd.batch, wd.dim, K - 1), dtype=torch.bfloat16, device="cuda") for _ in range(nstate)]
+    xs = [W.conv_decode_inputs(wd, k, device="cuda") for k in range(steps)]
+    outs = [torch.empty(wd.batch, wd.dim, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    for k in range(min(10, steps)):
+        ssm.conv1d_update(states[k % nstate], xs[k], wt, bias, out=outs[k % 2])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(steps):
+        ssm.conv1d_update(states[k % nstate], xs[k], wt, bias, out=outs[k % 2])
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    eager_ms = ev[0].elapsed_time(ev[steps]) / steps
+    # A step of this size runs for less time than a Python call takes to issue it, so the eager
+    # loop measures the host.  The same launches captured once in a HIP graph and replayed
+    # back to back measure the device.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for k in range(steps):
+                ssm.conv1d_update(states[k % nstate], xs[k], wt, bias, out=outs[k % 2])
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    gpu_ms = g0.elapsed_time(g1) / steps
+    bd = conv_step_bytes(wd, K)
+    dec = {"workload": "%s shape (%d x %d), width %d, bf16" % (wd.name, wd.batch, wd.dim, K), "steps": steps,
+           "rotated_state_buffers": nstate, "gpu_ms_per_step": gpu_ms, "timing": "HIP graph of the steps, replayed",
+           "eager_ms_per_step": eager_ms,
+           "roofline": {"bound": "hbm", "achieved": bd / (gpu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": bd / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                        "algorithmic_bytes_per_step": bd}}
+    return pre, dec
+
+
 def cpu_baseline(torch, x, w, seconds):
     """The fp64 oracle as it stands, on this host's cores, over the same inputs (repeated to ~seconds)."""
     sys.path.insert(0, ROOT)
@@ -191,6 +289,7 @@ def main():
     ap.add_argument("--workload", default="mamba130m", choices=["mamba130m", "mamba1p3b", "dna1m", "tiny"])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -247,6 +346,12 @@ def main():
         log("decode: %.4f ms/step wall, %.4f ms/step events, %.1f GB/s" % (d["ms_per_step"], d["gpu_ms_per_step"],
                                                                           d["roofline"]["achieved"]))
         res["decode"] = d
+    if not args.no_conv:
+        pre, dec = bench_conv(args, torch, ssm, W)
+        log("conv1d: %.4f ms/launch, %.1f GB/s; conv1d_update: %.4f ms/step, %.1f GB/s"
+            % (pre["launch_ms"], pre["roofline"]["achieved"], dec["gpu_ms_per_step"], dec["roofline"]["achieved"]))
+        res["conv1d"] = pre
+        res["conv1d_update"] = dec
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(torch, x0, w, args.cpu_seconds)
         log("cpu baseline: %.3e updates/s on %d threads" % (res["cpu_baseline"]["value"], res["cpu_baseline"]["cores"]))

@@ -52,7 +52,8 @@ struct ihipStream_t; /* hipStream_t is `struct ihipStream_t*` */
 typedef enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_NULL = 1,        /* a required pointer is NULL */
-  SSM_ERR_SHAPE = 2,       /* a size is out of range (batch/dim/seqlen < 1, dstate not in [1,64]) */
+  SSM_ERR_SHAPE = 2,       /* a size is out of range (batch/dim/seqlen < 1, dstate not in [1,64],
+                              conv width not in [1,4]) */
   SSM_ERR_DTYPE = 3,       /* io_dtype is not SSM_F32 or SSM_BF16 */
   SSM_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
   SSM_ERR_UNSUPPORTED = 5, /* unknown flag bits */
@@ -131,6 +132,39 @@ ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t 
                             const void* B, const void* C, const float* D,
                             const void* z, const float* delta_bias,
                             void* out, struct ihipStream_t* stream);
+
+/* The step that produces u: causal depthwise conv1d over time, plus a bias, then
+ * SiLU (ai.xwebgame.com Mamba page, the PyTorch block's step 2: a Conv1d with one
+ * group per channel and width-1 padding whose output is cut to the sequence
+ * length, followed by SiLU):
+ *   u[b,d,t] = silu(bias[d] + sum_{k<width} weight[d,k] * x[b,d,t-(width-1)+k])
+ * Inputs before step 0 are taken from initial_conv_state, else zero.
+ *   x, u               : [B, D, L]        io_dtype
+ *   weight             : [D, width]       fp32 (the page's Conv1d weight [D,1,width])
+ *   bias               : [D]              fp32, NULL means zero
+ *   initial_conv_state : [B, D, width-1]  io_dtype, the width-1 inputs before x,
+ *                        oldest first; NULL means zeros
+ *   final_conv_state   : [B, D, width-1]  io_dtype, the last width-1 inputs of the
+ *                        sequence initial_conv_state followed by x (what the next
+ *                        call or ssm_conv1d_update continues from); NULL means not
+ *                        written.  Must not overlap any input (use two buffers when
+ *                        processing a sequence in pieces).
+ * width must be in [1, 4] (the pages use 4); with width 1 the state pointers are
+ * ignored.  Other conventions as above (device pointers, 16-byte aligned bases,
+ * host-side checks, asynchronous on `stream`, u must not overlap any input). */
+ssm_status ssm_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
+                          int32_t io_dtype, const void* x, const float* weight,
+                          const float* bias, const void* initial_conv_state, void* u,
+                          void* final_conv_state, struct ihipStream_t* stream);
+
+/* One generation step of the same convolution: u = silu(bias + weight . (state, x)),
+ * then the state drops its oldest input and appends x (updated in place).
+ *   conv_state : [B, D, width-1] io_dtype, read and written (NULL allowed if width == 1)
+ *   x, u       : [B, D]          io_dtype
+ *   weight     : [D, width] fp32; bias : [D] fp32 or NULL */
+ssm_status ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int32_t io_dtype,
+                             void* conv_state, const void* x, const float* weight,
+                             const float* bias, void* u, struct ihipStream_t* stream);
 
 #ifdef __cplusplus
 }

@@ -1,13 +1,16 @@
 """MI355X (gfx950) selective state-space scan: HIP kernels behind a C ABI.
 
-    from selective_state_space_76_amd import scan_fwd, state_update
-    out, h_last = scan_fwd(u, delta, A, B, C, D, z, delta_bias)
-    y = state_update(state, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias)
+    from selective_state_space_76_amd import conv1d_fwd, scan_fwd, state_update, conv1d_update
+    u, conv_state = conv1d_fwd(x, conv_weight, conv_bias)          # the step that produces u
+    out, h_last = scan_fwd(u, delta, A, B, C, D, z, delta_bias)    # prefill
+    u_t = conv1d_update(conv_state, x_t, conv_weight, conv_bias)   # decode
+    y = state_update(h_last, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias)
 
 The C ABI is include/ssm_scan.h; the library is libssmscan.so in this package,
 built by `python -m selective_state_space_76_amd.build`.
 """
-from ._lib import (SSMError, load, scan_fwd, state_update, workspace_size, SSM_F32, SSM_BF16,  # noqa: F401
-                   SSM_FLAG_ZOH, SSM_FLAG_REVERSE, LIB_PATH)
+from ._lib import (SSMError, load, scan_fwd, state_update, conv1d_fwd, conv1d_update,  # noqa: F401
+                   workspace_size, SSM_F32, SSM_BF16, SSM_FLAG_ZOH, SSM_FLAG_REVERSE, LIB_PATH)
 
-__all__ = ["scan_fwd", "state_update", "workspace_size", "load", "SSMError", "LIB_PATH"]
+__all__ = ["scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "load", "SSMError",
+           "LIB_PATH"]

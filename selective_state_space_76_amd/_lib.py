@@ -35,7 +35,8 @@ class ssm_shape(ctypes.Structure):
 
 
 _lib = None
-EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update")
+EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update",
+           "ssm_conv1d_fwd", "ssm_conv1d_update")
 
 
 def load() -> ctypes.CDLL:
@@ -58,6 +59,10 @@ def load() -> ctypes.CDLL:
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, u32] + [vp] * 10 + [vp]
     lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 6 + [vp]
+    lib.ssm_conv1d_fwd.restype = ctypes.c_int
+    lib.ssm_conv1d_update.argtypes = [i64, i64, i64, i32] + [vp] * 5 + [vp]
+    lib.ssm_conv1d_update.restype = ctypes.c_int
     if lib.ssm_abi_version() != ABI_VERSION:
         raise ImportError("libssmscan.so ABI version %d, binding expects %d" % (lib.ssm_abi_version(), ABI_VERSION))
     _lib = lib
@@ -87,6 +92,17 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t, shape, dtype, name):
+    """The C ABI trusts sizes and element types; check them here so a mismatched tensor
+    is an error, not an out-of-bounds read."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
 
 
 def _stream(stream):
@@ -125,6 +141,15 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
         final_state = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=u.device)
     elif final_state is False:
         final_state = None
+    f32 = torch.float32
+    for t, shp, dt, name in ((delta, (Bsz, Dm, L), u.dtype, "delta"), (A, (Dm, N), f32, "A"),
+                             (B, (Bsz, N, L), u.dtype, "B"), (C, (Bsz, N, L), u.dtype, "C"),
+                             (D, (Dm,), f32, "D"), (z, (Bsz, Dm, L), u.dtype, "z"),
+                             (delta_bias, (Dm,), f32, "delta_bias"),
+                             (initial_state, (Bsz, Dm, N), f32, "initial_state"),
+                             (out, (Bsz, Dm, L), u.dtype, "out"),
+                             (final_state, (Bsz, Dm, N), f32, "final_state")):
+        _expect(t, shp, dt, name)
     ws_bytes = 0
     if split:
         need = int(lib.ssm_scan_workspace_size(ctypes.byref(sh)))
@@ -150,7 +175,58 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     io = _io_dtype(u)
     if out is None:
         out = torch.empty_like(u)
+    f32 = torch.float32
+    for t, shp, dt, name in ((state, (Bsz, Dm, N), f32, "state"), (delta, (Bsz, Dm), u.dtype, "delta"),
+                             (A, (Dm, N), f32, "A"), (B, (Bsz, N), u.dtype, "B"), (C, (Bsz, N), u.dtype, "C"),
+                             (D, (Dm,), f32, "D"), (z, (Bsz, Dm), u.dtype, "z"),
+                             (delta_bias, (Dm,), f32, "delta_bias"), (out, (Bsz, Dm), u.dtype, "out")):
+        _expect(t, shp, dt, name)
     _check(lib.ssm_state_update(Bsz, Dm, N, io, SSM_FLAG_ZOH if zoh else 0, _ptr(state), _ptr(u), _ptr(delta),
                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
                                 _stream(stream)))
+    return out
+
+
+def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_state=True, stream=None):
+    """Causal depthwise conv1d + bias + SiLU, producing u.  x: [B,D,L] fp32/bf16; weight: [D,K]
+    fp32 (K in 1..4); bias: [D] fp32 or None; initial_state: [B,D,K-1] in x's dtype or None.
+    Returns (u [B,D,L], final_state [B,D,K-1] or None).  final_state may be True (allocate),
+    False/None (not written) or a tensor (not overlapping initial_state)."""
+    lib = load()
+    Bsz, Dm, L = x.shape
+    K = weight.shape[1]
+    io = _io_dtype(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is True:
+        final_state = torch.empty((Bsz, Dm, K - 1), dtype=x.dtype, device=x.device)
+    elif final_state is False:
+        final_state = None
+    f32 = torch.float32
+    for t, shp, dt, name in ((weight, (Dm, K), f32, "weight"), (bias, (Dm,), f32, "bias"),
+                             (initial_state, (Bsz, Dm, K - 1), x.dtype, "initial_state"),
+                             (out, (Bsz, Dm, L), x.dtype, "out"),
+                             (final_state, (Bsz, Dm, K - 1), x.dtype, "final_state")):
+        _expect(t, shp, dt, name)
+    _check(lib.ssm_conv1d_fwd(Bsz, Dm, L, K, io, _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state),
+                              _ptr(out), _ptr(final_state), _stream(stream)))
+    return out, final_state
+
+
+def conv1d_update(conv_state, x, weight, bias=None, *, out=None, stream=None):
+    """One decode step of the conv: conv_state [B,D,K-1] (x's dtype) updated in place;
+    x: [B,D].  Returns u [B,D]."""
+    lib = load()
+    Bsz, Dm = x.shape
+    K = weight.shape[1]
+    io = _io_dtype(x)
+    if out is None:
+        out = torch.empty_like(x)
+    f32 = torch.float32
+    for t, shp, dt, name in ((conv_state, (Bsz, Dm, K - 1), x.dtype, "conv_state"),
+                             (weight, (Dm, K), f32, "weight"), (bias, (Dm,), f32, "bias"),
+                             (out, (Bsz, Dm), x.dtype, "out")):
+        _expect(t, shp, dt, name)
+    _check(lib.ssm_conv1d_update(Bsz, Dm, K, io, _ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias),
+                                 _ptr(out), _stream(stream)))
     return out

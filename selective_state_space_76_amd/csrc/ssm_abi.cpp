@@ -92,7 +92,8 @@ const char* ssm_status_str(int status) {
   switch (status) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "a required pointer is NULL";
-    case SSM_ERR_SHAPE: return "a size is out of range (batch, dim, seqlen >= 1; dstate in [1, 64])";
+    case SSM_ERR_SHAPE:
+      return "a size is out of range (batch, dim, seqlen >= 1; dstate in [1, 64]; conv width in [1, 4])";
     case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case SSM_ERR_UNSUPPORTED: return "unknown flag bits";
@@ -213,6 +214,68 @@ ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t 
   p.vec = (dstate % 4) == 0 ? 1 : 0;
   p.zoh = (flags & SSM_FLAG_ZOH) ? 1 : 0;
   return launch_status(ssm::launch_step(p, io_dtype == SSM_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ssm_status ssm_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int32_t io_dtype,
+                          const void* x, const float* weight, const float* bias,
+                          const void* initial_conv_state, void* u, void* final_conv_state,
+                          struct ihipStream_t* stream) {
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (batch < 1 || dim < 1 || seqlen < 1 || width < 1 || width > 4) return SSM_ERR_SHAPE;
+  if (batch > kMaxDim || dim > kMaxDim || seqlen > kMaxDim) return SSM_ERR_SHAPE;
+  int64_t bd, bdl;
+  if (!mul_ok(batch, dim, &bd) || !mul_ok(bd, seqlen, &bdl)) return SSM_ERR_SHAPE;
+  if (bdl > (int64_t(1) << 31) * 255) return SSM_ERR_SHAPE;  // grid of the per-element path
+  if (!x || !weight || !u) return SSM_ERR_NULL;
+  const int64_t H = width - 1;
+  const void* st_in = H > 0 ? initial_conv_state : nullptr;
+  void* st_out = H > 0 ? final_conv_state : nullptr;
+  const void* ptrs[] = {x, weight, bias, st_in, u, st_out};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return SSM_ERR_ALIGN;
+  const int64_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const Range ins[] = {span(x, bdl, es), span(weight, dim * width, 4), span(bias, bias ? dim : 0, 4),
+                       span(st_in, st_in ? bd * H : 0, es)};
+  const Range ru = span(u, bdl, es), rs = span(st_out, st_out ? bd * H : 0, es);
+  for (const Range& r : ins)
+    if (overlaps(ru, r) || overlaps(rs, r)) return SSM_ERR_OVERLAP;
+  if (overlaps(ru, rs)) return SSM_ERR_OVERLAP;
+
+  ssm::ConvParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.w = weight; p.bias = bias; p.state_in = st_in; p.u = u; p.state_out = st_out;
+  p.Bsz = batch; p.Dm = dim; p.L = seqlen; p.K = (int)width;
+  const int64_t V = 16 / es;  // elements per 16-byte chunk
+  const int mode = (seqlen % V) == 0 ? 1 : 0;
+  return launch_status(ssm::launch_conv(p, io_dtype == SSM_BF16, mode, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ssm_status ssm_conv1d_update(int64_t batch, int64_t dim, int64_t width, int32_t io_dtype, void* conv_state,
+                             const void* x, const float* weight, const float* bias, void* u,
+                             struct ihipStream_t* stream) {
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (batch < 1 || dim < 1 || width < 1 || width > 4 || batch > kMaxDim || dim > kMaxDim) return SSM_ERR_SHAPE;
+  int64_t bd;
+  if (!mul_ok(batch, dim, &bd)) return SSM_ERR_SHAPE;
+  if (bd > (int64_t(1) << 31) * 255) return SSM_ERR_SHAPE;
+  const int64_t H = width - 1;
+  void* st = H > 0 ? conv_state : nullptr;
+  if (!x || !weight || !u || (H > 0 && !st)) return SSM_ERR_NULL;
+  const void* ptrs[] = {st, x, weight, bias, u};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return SSM_ERR_ALIGN;
+  const int64_t es = io_dtype == SSM_BF16 ? 2 : 4;
+  const Range ins[] = {span(x, bd, es), span(weight, dim * width, 4), span(bias, bias ? dim : 0, 4)};
+  const Range ru = span(u, bd, es), rs = span(st, st ? bd * H : 0, es);
+  for (const Range& r : ins)
+    if (overlaps(ru, r) || overlaps(rs, r)) return SSM_ERR_OVERLAP;
+  if (overlaps(ru, rs)) return SSM_ERR_OVERLAP;
+
+  ssm::ConvParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.w = weight; p.bias = bias; p.state_in = st; p.u = u; p.state_out = st;
+  p.Bsz = batch; p.Dm = dim; p.L = 1; p.K = (int)width;
+  return launch_status(ssm::launch_conv(p, io_dtype == SSM_BF16, 2, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -46,7 +46,20 @@ struct StepParams {
   int zoh;
 };
 
+struct ConvParams {
+  const void* x;          // [B,D,L] (decode: [B,D])
+  const float* w;         // [D,K]
+  const float* bias;      // [D] or null
+  const void* state_in;   // [B,D,K-1] inputs before x, or null (zeros)
+  void* u;                // [B,D,L] (decode: [B,D])
+  void* state_out;        // [B,D,K-1] or null; decode: the state, read and written
+  int64_t Bsz, Dm, L;
+  int K;                  // width, 1..4
+};
+
 hipError_t launch_scan(const ScanParams& p, bool bf16, int mode, hipStream_t s);
+// mode 0: per-element prefill, 1: 16-byte-chunk prefill (L a multiple of the chunk), 2: decode step
+hipError_t launch_conv(const ConvParams& p, bool bf16, int mode, hipStream_t s);
 hipError_t launch_carry(const ScanParams& p, hipStream_t s);
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
 

@@ -20,6 +20,12 @@ dt_bias = softplus^-1(Delta*), Delta* log-uniform in [1e-3, 1e-1];
 A[d, n] = -(n + 1); B, C ~ N(0,1) per (batch, state, step), shared by channels;
 D = 1.  bf16 tensors are drawn in fp32 and rounded once (round-to-nearest-even).
 
+The conv step that produces u (conv_inputs / conv_decode_inputs) takes the
+same shapes: its input x ~ N(0,1) [B,D,L]; weight [D,K] and bias [D] drawn
+uniform in +-1/sqrt(K) (the default initialisation of a depthwise Conv1d of
+width K, the layer of the pages' PyTorch block); the carried state, when one is
+used, ~ N(0,1).
+
 Random numbers come from torch generators seeded per (workload seed, tensor id,
 step), on the device the tensors are created on.
 """
@@ -67,7 +73,8 @@ WORKLOADS = {
 }
 
 # tensor ids used to derive independent generator streams
-_TID = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "bias": 6, "emb": 7, "tok": 8, "noise": 9}
+_TID = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "bias": 6, "emb": 7, "tok": 8, "noise": 9,
+        "cx": 10, "cw": 11, "cb": 12, "cst": 13}
 
 
 def _gen(device, seed: int, tid: str, step: int = 0) -> torch.Generator:
@@ -146,3 +153,32 @@ def decode_inputs(w: Workload, step: int, device="cpu"):
         B=_normal((w.batch, w.dstate), device, w.seed, "B", step).to(dt),
         C=_normal((w.batch, w.dstate), device, w.seed, "C", step).to(dt),
     )
+
+
+def _uniform(shape, device, seed, tid, bound, step=0):
+    g = _gen(device, seed, tid, step)
+    return (torch.rand(shape, generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0) * bound
+
+
+def conv_params(w: Workload, width: int = 4, device="cpu"):
+    """Conv weight [D, width] and bias [D], fp32, uniform in +-1/sqrt(width)."""
+    bound = 1.0 / math.sqrt(width)
+    return (_uniform((w.dim, width), device, w.seed, "cw", bound),
+            _uniform((w.dim,), device, w.seed, "cb", bound))
+
+
+def conv_inputs(w: Workload, width: int = 4, device="cpu", state: bool = False):
+    """Inputs of one conv call: dict with x [B,D,L] (io dtype), weight, bias and, if asked,
+    state [B,D,width-1] (io dtype)."""
+    dt = w.torch_dtype
+    x = _normal((w.batch, w.dim, w.seqlen), device, w.seed, "cx").to(dt)
+    weight, bias = conv_params(w, width, device)
+    out = dict(x=x, weight=weight, bias=bias)
+    if state:
+        out["state"] = _normal((w.batch, w.dim, width - 1), device, w.seed, "cst").to(dt)
+    return out
+
+
+def conv_decode_inputs(w: Workload, step: int, device="cpu"):
+    """Per-token conv input x [B,D] of decode step `step`."""
+    return _normal((w.batch, w.dim), device, w.seed, "cx", step).to(w.torch_dtype)

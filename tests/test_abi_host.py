@@ -22,7 +22,7 @@ def fake(i, off=0):
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -132,3 +132,45 @@ def test_state_update_errors():
     assert step(u=fake(2, off=2)) == 4
     assert step(out=fake(2, off=16)) == 8    # out inside u
     assert step(state=fake(4, off=0)) == 8   # state on top of A
+
+
+def conv(batch=2, dim=8, seqlen=64, width=4, io=L.SSM_BF16, **kw):
+    lib = L.load()
+    p = dict(x=fake(1), w=fake(2), bias=None, st_in=None, u=fake(3), st_out=None)
+    p.update(kw)
+    return lib.ssm_conv1d_fwd(batch, dim, seqlen, width, io, p["x"], p["w"], p["bias"], p["st_in"],
+                              p["u"], p["st_out"], None)
+
+
+def conv_upd(batch=2, dim=8, width=4, io=L.SSM_BF16, **kw):
+    lib = L.load()
+    p = dict(st=fake(1), x=fake(2), w=fake(3), bias=None, u=fake(4))
+    p.update(kw)
+    return lib.ssm_conv1d_update(batch, dim, width, io, p["st"], p["x"], p["w"], p["bias"], p["u"], None)
+
+
+def test_conv_errors():
+    assert conv(io=2) == 3
+    for bad in (dict(batch=0), dict(dim=0), dict(seqlen=0), dict(width=0), dict(width=5), dict(seqlen=1 << 41)):
+        assert conv(**bad) == 2, bad
+    for name in ("x", "w", "u"):
+        assert conv(**{name: None}) == 1, name
+    assert conv(x=fake(1, off=2)) == 4
+    assert conv(bias=fake(5, off=4)) == 4
+    assert conv(st_in=fake(6, off=8)) == 4
+    assert conv(u=fake(1, off=32)) == 8                        # u inside x
+    assert conv(st_out=fake(6), st_in=fake(6)) == 8            # state out over state in
+    assert conv(st_out=fake(3, off=64)) == 8                   # state out inside u
+    assert conv(st_out=fake(2)) == 8                           # state out over the weights
+
+
+def test_conv_update_errors():
+    assert conv_upd(io=5) == 3
+    for bad in (dict(batch=0), dict(dim=-1), dict(width=0), dict(width=7)):
+        assert conv_upd(**bad) == 2, bad
+    for name in ("st", "x", "w", "u"):
+        assert conv_upd(**{name: None}) == 1, name
+    assert conv_upd(st=fake(1, off=6)) == 4
+    assert conv_upd(u=fake(2, off=16)) == 8      # u inside x
+    assert conv_upd(st=fake(3)) == 8             # state over the weights
+    assert conv_upd(u=fake(1, off=16)) == 8      # u inside the state
