@@ -18,7 +18,9 @@ What it computes follows the pages' definition of the selective SSM:
     initial state (mlqm.cn article, section 6.2, chunked long sequences);
   * the step that produces u: causal depthwise conv1d of width K with a bias,
     cut to the sequence length, then SiLU (ai.xwebgame.com Mamba page, the
-    PyTorch block's step 2).
+    PyTorch block's step 2);
+  * the gradients of the scan: not on the pages; the chain rule applied to the
+    definition above, as a reverse-time adjoint recurrence (scan_bwd).
 """
 from __future__ import annotations
 
@@ -59,6 +61,8 @@ class Oracle:
         lib.oracle_step_f64.restype = ctypes.c_int
         lib.oracle_conv1d_f64.argtypes = [i64, i64, i64, i64] + [d] * 6 + [ctypes.c_int]
         lib.oracle_conv1d_f64.restype = ctypes.c_int
+        lib.oracle_scan_bwd_f64.argtypes = [i64, i64, i64, i64] + [d] * 20 + [ctypes.c_int, ctypes.c_int]
+        lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         self.lib = lib
 
     def scan(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
@@ -103,6 +107,38 @@ class Oracle:
         if rc != 0:
             raise RuntimeError("oracle_step_f64 failed (%d)" % rc)
         return out, st
+
+    def scan_bwd(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dout,
+                 dfinal=None, reverse=False, threads=0):
+        """Gradients of the scan for output gradient dout [Bsz,Dm,L] (and final-state gradient
+        dfinal [Bsz,Dm,N] or None).  Returns a dict with du, ddelta, dA, dB, dC and, when the
+        matching input is given, dD, dz, ddelta_bias, dh0 (dh0 always: the gradient of the
+        state before the first step)."""
+        u, delta, A, B, C, dout = map(_f64, (u, delta, A, B, C, dout))
+        D, z, delta_bias, h0, dfinal = map(_f64, (D, z, delta_bias, h0, dfinal))
+        Bsz, Dm, L = u.shape
+        N = A.shape[1]
+        assert delta.shape == u.shape and dout.shape == u.shape and A.shape == (Dm, N)
+        assert B.shape == (Bsz, N, L) and C.shape == (Bsz, N, L)
+        assert dfinal is None or dfinal.shape == (Bsz, Dm, N)
+        g = dict(du=np.empty((Bsz, Dm, L)), ddelta=np.empty((Bsz, Dm, L)), dA=np.empty((Dm, N)),
+                 dB=np.empty((Bsz, N, L)), dC=np.empty((Bsz, N, L)), dD=np.empty(Dm),
+                 dz=np.empty((Bsz, Dm, L)) if z is not None else None, ddelta_bias=np.empty(Dm),
+                 dh0=np.empty((Bsz, Dm, N)))
+        rc = self.lib.oracle_scan_bwd_f64(
+            Bsz, Dm, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), _ptr(h0), _ptr(dout), _ptr(dfinal), _ptr(g["du"]), _ptr(g["ddelta"]),
+            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+            _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), REVERSE if reverse else 0, int(threads))
+        if rc != 0:
+            raise RuntimeError("oracle_scan_bwd_f64 failed (%d)" % rc)
+        if D is None:
+            g["dD"] = None
+        if delta_bias is None:
+            g["ddelta_bias"] = None
+        if z is None:
+            g["dz"] = None
+        return g
 
     def conv1d(self, x, w, bias=None, state=None, threads=0):
         """Causal depthwise conv1d + bias + SiLU in fp64.
@@ -174,6 +210,10 @@ def step(*args, **kw):
 
 def conv1d(*args, **kw):
     return default().conv1d(*args, **kw)
+
+
+def scan_bwd(*args, **kw):
+    return default().scan_bwd(*args, **kw)
 
 
 def conv_step(*args, **kw):

@@ -37,6 +37,10 @@
  *   u, delta, z, out : [Bsz, Dm, L]     B, C : [Bsz, N, L]
  *   A : [Dm, N]   D, bias : [Dm]   h0, final_state : [Bsz, Dm, N]
  *
+ * The backward pass (oracle_scan_bwd_f64) is not described on the pages; it is
+ * the chain rule applied to the forward definition above, written as the
+ * reverse-time adjoint recurrence (see the comment on that function).
+ *
  * The step that produces u (oracle_conv1d_f64) follows the block of [xw-code]:
  * a depthwise 1-D convolution of width K over time with K-1 zeros of padding
  * on the left, its output cut to the first L steps (so step t only sees steps
@@ -60,7 +64,7 @@ static double softplus_f64(double x) {
 
 static double silu_f64(double z) { return z / (1.0 + exp(-z)); }
 
-int oracle_abi_version(void) { return 3; }
+int oracle_abi_version(void) { return 4; }
 
 /* Threads an OpenMP region of the oracle uses by default (1 without OpenMP). */
 int oracle_max_threads(void) {
@@ -200,5 +204,156 @@ int oracle_conv1d_f64(int64_t Bsz, int64_t Dm, int64_t L, int64_t K,
       for (int64_t j = 0; j < H; ++j) state_out[r * H + j] = xe[L + j];
     free(xe);
   }
+  return bad ? -1 : 0;
+}
+
+/* Gradients of the scan (default discretisation B_bar = dt*B; REVERSE allowed) for a
+ * given output gradient dout [Bsz,Dm,L] and optional final-state gradient dfs
+ * [Bsz,Dm,N].  Derived with the chain rule from the forward definition; with
+ * G_n the gradient reaching h_n after step t (time order of the scan):
+ *   dy_t   = dout_t * silu(z_t)                     (dout_t without z)
+ *   dz_t   = dout_t * y_t * s(z_t) * (1 + z_t (1 - s(z_t))),  s = logistic
+ *   G_n   += dy_t * C[n,t];   dC[b,n,t] += dy_t * h_t[n]
+ *   du_t   = dy_t * D + sum_n G_n * dt_t * B[n,t]
+ *   dD    += dy_t * u_t
+ *   ddt_t  = sum_n G_n * (h_{t-1}[n] * Abar * A[n] + u_t * B[n,t])
+ *   dA[n] += G_n * h_{t-1}[n] * Abar * dt_t
+ *   dB[b,n,t] += G_n * dt_t * u_t
+ *   G_n    = G_n * Abar                             (on to h_{t-1})
+ *   ddelta_t = ddt_t * s(x_t)   (softplus' = logistic);  dbias += ddelta_t
+ *   dh0 = G after step 0 of the scan order.
+ * Outputs: du, ddelta : [Bsz,Dm,L]; dz : [Bsz,Dm,L] (only when z is given);
+ * dA : [Dm,N]; dB, dC : [Bsz,N,L]; dD, dbias : [Dm] (may be NULL); dh0 : [Bsz,Dm,N]
+ * (may be NULL).  Sums over channels and batch rows are taken in a fixed order. */
+int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
+                        const double* u, const double* delta, const double* A,
+                        const double* Bm, const double* Cm, const double* Dv,
+                        const double* z, const double* bias, const double* h0,
+                        const double* dout, const double* dfs,
+                        double* du, double* ddelta, double* dA, double* dB, double* dC,
+                        double* dD, double* dz, double* dbias, double* dh0,
+                        int flags, int nthreads) {
+  if (Bsz < 0 || Dm < 0 || N <= 0 || L < 0) return -1;
+  if (!u || !delta || !A || !Bm || !Cm || !dout || !du || !ddelta || !dA || !dB || !dC) return -1;
+  if (z && !dz) return -1;
+  if (flags & ORACLE_ZOH) return -1;
+  const int64_t rows = Bsz * Dm;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  /* per-row contributions to the channel and batch sums, reduced afterwards in row order */
+  double* rA = (double*)calloc((size_t)(rows * N), sizeof(double));
+  double* rD = (double*)calloc((size_t)rows, sizeof(double));
+  double* rb = (double*)calloc((size_t)rows, sizeof(double));
+  if (!rA || !rD || !rb) { free(rA); free(rD); free(rb); return -1; }
+  for (int64_t i = 0; i < Bsz * N * L; ++i) { dB[i] = 0.0; dC[i] = 0.0; }
+  int bad = 0;
+  /* channels are taken in fixed chunks of CH; each chunk sums its channels' dB/dC
+   * contributions in channel order into its own slab, and the slabs are added in chunk
+   * order, so the result does not depend on the number of threads */
+  const int64_t CH = 64;
+  const int64_t nch = (Dm + CH - 1) / CH;
+  double* slab = (double*)malloc((size_t)(nch > 0 ? nch : 1) * (size_t)(2 * N * (L > 0 ? L : 1)) * sizeof(double));
+  if (!slab) { free(rA); free(rD); free(rb); return -1; }
+  for (int64_t b = 0; b < Bsz && !bad; ++b) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nch; ++c) {
+      double* sB = slab + c * 2 * N * L;
+      double* sC = sB + N * L;
+      for (int64_t i = 0; i < N * L; ++i) { sB[i] = 0.0; sC[i] = 0.0; }
+      double* hs = (double*)malloc((size_t)((L + 1) * N) * sizeof(double)); /* state before each step */
+      double* ys = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+      double* G = (double*)malloc((size_t)N * sizeof(double));
+      if (!hs || !ys || !G) { bad = 1; free(hs); free(ys); free(G); continue; }
+      for (int64_t d = c * CH; d < Dm && d < (c + 1) * CH; ++d) {
+        const int64_t r = b * Dm + d;
+        const double* ur = u + r * L;
+        const double* dr = delta + r * L;
+        const double* zr = z ? z + r * L : NULL;
+        const double* Ab = Bm + b * N * L;
+        const double* Cb = Cm + b * N * L;
+        const double bd = bias ? bias[d] : 0.0;
+        const double Dd = Dv ? Dv[d] : 0.0;
+        /* forward, keeping every state: hs[s*N + n] is the state before scan step s */
+        for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[r * N + n] : 0.0;
+        for (int64_t s = 0; s < L; ++s) {
+          const int64_t t = (flags & ORACLE_REVERSE) ? (L - 1 - s) : s;
+          const double dt = softplus_f64(dr[t] + bd);
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double a = exp(dt * A[d * N + n]);
+            const double h = a * hs[s * N + n] + dt * Ab[n * L + t] * ur[t];
+            hs[(s + 1) * N + n] = h;
+            acc += Cb[n * L + t] * h;
+          }
+          ys[t] = acc + Dd * ur[t];
+        }
+        /* backward in reverse scan order */
+        for (int64_t n = 0; n < N; ++n) G[n] = dfs ? dfs[r * N + n] : 0.0;
+        double accD = 0.0, accb = 0.0;
+        for (int64_t s = L - 1; s >= 0; --s) {
+          const int64_t t = (flags & ORACLE_REVERSE) ? (L - 1 - s) : s;
+          const double x = dr[t] + bd;
+          const double dt = softplus_f64(x);
+          double dy = dout[r * L + t];
+          if (zr) {
+            const double sg = 1.0 / (1.0 + exp(-zr[t]));
+            dz[r * L + t] = dout[r * L + t] * ys[t] * sg * (1.0 + zr[t] * (1.0 - sg));
+            dy = dout[r * L + t] * silu_f64(zr[t]);
+          }
+          double dut = dy * Dd;
+          double ddt = 0.0;
+          accD += dy * ur[t];
+          for (int64_t n = 0; n < N; ++n) {
+            const double an = A[d * N + n];
+            const double a = exp(dt * an);
+            const double hp = hs[s * N + n];
+            G[n] += dy * Cb[n * L + t];
+            sC[n * L + t] += dy * hs[(s + 1) * N + n];
+            dut += G[n] * dt * Ab[n * L + t];
+            ddt += G[n] * (hp * a * an + ur[t] * Ab[n * L + t]);
+            rA[r * N + n] += G[n] * hp * a * dt;
+            sB[n * L + t] += G[n] * dt * ur[t];
+            G[n] *= a;
+          }
+          du[r * L + t] = dut;
+          const double dx = ddt / (1.0 + exp(-x));
+          ddelta[r * L + t] = dx;
+          accb += dx;
+        }
+        rD[r] = accD;
+        rb[r] = accb;
+        if (dh0)
+          for (int64_t n = 0; n < N; ++n) dh0[r * N + n] = G[n];
+      }
+      free(hs); free(ys); free(G);
+    }
+    if (!bad)
+      for (int64_t c = 0; c < nch; ++c) {
+        const double* sB = slab + c * 2 * N * L;
+        const double* sC = sB + N * L;
+        for (int64_t i = 0; i < N * L; ++i) {
+          dB[b * N * L + i] += sB[i];
+          dC[b * N * L + i] += sC[i];
+        }
+      }
+  }
+  free(slab);
+  if (!bad) {
+    for (int64_t d = 0; d < Dm; ++d) {
+      for (int64_t n = 0; n < N; ++n) {
+        double s = 0.0;
+        for (int64_t b = 0; b < Bsz; ++b) s += rA[(b * Dm + d) * N + n];
+        dA[d * N + n] = s;
+      }
+      double sD = 0.0, sb = 0.0;
+      for (int64_t b = 0; b < Bsz; ++b) { sD += rD[b * Dm + d]; sb += rb[b * Dm + d]; }
+      if (dD) dD[d] = sD;
+      if (dbias) dbias[d] = sb;
+    }
+  }
+  free(rA); free(rD); free(rb);
   return bad ? -1 : 0;
 }

@@ -26,7 +26,10 @@ MUTANTS = [
     ("input_u_dropped", "h[n] = abar * h[n] + bbar * ur[t];", "h[n] = abar * h[n] + bbar;"),
     ("C_off_by_one", "acc += Cb[n * L + t] * h[n];", "acc += Cb[n * L + (t > 0 ? t - 1 : 0)] * h[n];"),
     ("initial_state_ignored", "h[n] = h0 ? h0[r * N + n] : 0.0;", "h[n] = 0.0;"),
-    ("reverse_ignored", "(flags & ORACLE_REVERSE) ? (L - 1 - s) : s", "s"),
+    ("reverse_ignored", "(flags & ORACLE_REVERSE) ? (L - 1 - s) : s;\n      const double dt = softplus_f64(dr[t] + (bias ? bias[d] : 0.0));",
+     "s;\n      const double dt = softplus_f64(dr[t] + (bias ? bias[d] : 0.0));"),
+    ("bwd_reverse_ignored", "(flags & ORACLE_REVERSE) ? (L - 1 - s) : s;\n          const double x = dr[t] + bd;",
+     "s;\n          const double x = dr[t] + bd;"),
     ("zoh_sign", "bbar = (abar - 1.0) / a_dn * Ab[n * L + t];", "bbar = (1.0 - abar) / a_dn * Ab[n * L + t];"),
     ("step_drops_u", "*h = abar * *h + bbar * u[r];", "*h = abar * *h + bbar;"),
     ("A_transposed", "const double a_dn = A[d * N + n];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab",
@@ -46,6 +49,18 @@ MUTANTS = [
     ("conv_state_out_shifted", "state_out[r * H + j] = xe[L + j];",
      "state_out[r * H + j] = xe[L + j > 0 ? L + j - 1 : 0];"),
     ("conv_weight_row_stride", "v += w[d * K + k] * xe[t + k];", "v += w[k * Dm + d] * xe[t + k];"),
+    ("bwd_adjoint_not_decayed", "          G[n] *= a;\n", "\n"),
+    ("bwd_dC_uses_old_state", "sC[n * L + t] += dy * hs[(s + 1) * N + n];", "sC[n * L + t] += dy * hs[s * N + n];"),
+    ("bwd_dB_drops_u", "sB[n * L + t] += G[n] * dt * ur[t];", "sB[n * L + t] += G[n] * dt;"),
+    ("bwd_dA_drops_dt", "rA[r * N + n] += G[n] * hp * a * dt;", "rA[r * N + n] += G[n] * hp * a;"),
+    ("bwd_softplus_derivative", "const double dx = ddt / (1.0 + exp(-x));", "const double dx = ddt;"),
+    ("bwd_ddt_drops_decay_term", "ddt += G[n] * (hp * a * an + ur[t] * Ab[n * L + t]);",
+     "ddt += G[n] * (ur[t] * Ab[n * L + t]);"),
+    ("bwd_dz_silu_derivative", "sg * (1.0 + zr[t] * (1.0 - sg));", "sg;"),
+    ("bwd_du_drops_skip", "double dut = dy * Dd;", "double dut = 0.0;"),
+    ("bwd_adjoint_seed_ignored", "G[n] = dfs ? dfs[r * N + n] : 0.0;", "G[n] = 0.0;"),
+    ("bwd_dy_ungated", "dy = dout[r * L + t] * silu_f64(zr[t]);", "dy = dout[r * L + t];"),
+    ("bwd_adjoint_before_C", "G[n] += dy * Cb[n * L + t];\n            sC", "G[n] += 0.0 * Cb[n * L + t];\n            sC"),
 ]
 
 
