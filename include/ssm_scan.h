@@ -133,6 +133,43 @@ ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t 
                             const void* z, const float* delta_bias,
                             void* out, struct ihipStream_t* stream);
 
+/* Bytes of device workspace ssm_scan_bwd needs for this shape (0 for an invalid
+ * shape): block checkpoints of the state, B*D*ceil(L/64)*N fp32; per-workgroup
+ * partial sums of dB and dC, 2*ceil(D/16)*B*N*L fp32; and the per-batch-row
+ * partial sums of dA, dD and ddelta_bias. */
+size_t ssm_scan_bwd_workspace_size(const ssm_shape* shape);
+
+/* Gradients of ssm_scan_fwd (training backward pass).  The pages describe only the
+ * forward recurrence; these are its exact derivatives by the chain rule (the
+ * reverse-time adjoint recurrence), computed from the forward inputs alone: the
+ * forward states are recomputed from checkpoints, nothing from the forward call
+ * is needed.
+ *   Inputs: the forward's inputs (same layouts, same NULL rules) plus
+ *   dout             : [B, D, L] io_dtype, gradient of out
+ *   dfinal_state     : [B, D, N] fp32 gradient of final_state, NULL means zero
+ *   Outputs (all fully written):
+ *   du, ddelta       : [B, D, L] io_dtype
+ *   dA               : [D, N]    fp32, summed over batch rows and steps
+ *   dB, dC           : [B, N, L] fp32, summed over channels
+ *   dD, ddelta_bias  : [D]       fp32, NULL means not computed (written even when
+ *                      D / delta_bias is NULL: the gradient at zero)
+ *   dz               : [B, D, L] io_dtype, required when z is given, else ignored
+ *   dinitial_state   : [B, D, N] fp32 gradient of initial_state, NULL means not written
+ *   workspace        : required, at least ssm_scan_bwd_workspace_size() bytes
+ * shape->flags may hold SSM_FLAG_REVERSE; SSM_FLAG_ZOH is SSM_ERR_UNSUPPORTED.
+ * No output may overlap an input, another output or the workspace.  Every sum is
+ * taken in a fixed order, so results are bitwise reproducible. */
+ssm_status ssm_scan_bwd(const ssm_shape* shape,
+                        const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D,
+                        const void* z, const float* delta_bias,
+                        const float* initial_state,
+                        const void* dout, const float* dfinal_state,
+                        void* du, void* ddelta, float* dA, float* dB, float* dC,
+                        float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
+                        void* workspace, size_t workspace_bytes,
+                        struct ihipStream_t* stream);
+
 /* The step that produces u: causal depthwise conv1d over time, plus a bias, then
  * SiLU (ai.xwebgame.com Mamba page, the PyTorch block's step 2: a Conv1d with one
  * group per channel and width-1 padding whose output is cut to the sequence

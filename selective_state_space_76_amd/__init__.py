@@ -3,6 +3,7 @@
     from selective_state_space_76_amd import conv1d_fwd, scan_fwd, state_update, conv1d_update
     u, conv_state = conv1d_fwd(x, conv_weight, conv_bias)          # the step that produces u
     out, h_last = scan_fwd(u, delta, A, B, C, D, z, delta_bias)    # prefill
+    grads = scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout=g)  # training backward
     u_t = conv1d_update(conv_state, x_t, conv_weight, conv_bias)   # decode
     y = state_update(h_last, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias)
 
@@ -10,7 +11,7 @@ The C ABI is include/ssm_scan.h; the library is libssmscan.so in this package,
 built by `python -m selective_state_space_76_amd.build`.
 """
 from ._lib import (SSMError, load, scan_fwd, state_update, conv1d_fwd, conv1d_update,  # noqa: F401
-                   workspace_size, SSM_F32, SSM_BF16, SSM_FLAG_ZOH, SSM_FLAG_REVERSE, LIB_PATH)
+                   scan_bwd, bwd_workspace_size, workspace_size, SSM_F32, SSM_BF16, SSM_FLAG_ZOH, SSM_FLAG_REVERSE, LIB_PATH)
 
-__all__ = ["scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "load", "SSMError",
-           "LIB_PATH"]
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size",
+           "bwd_workspace_size", "load", "SSMError", "LIB_PATH"]

@@ -36,7 +36,7 @@ class ssm_shape(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update",
-           "ssm_conv1d_fwd", "ssm_conv1d_update")
+           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_conv1d_fwd", "ssm_conv1d_update")
 
 
 def load() -> ctypes.CDLL:
@@ -59,6 +59,10 @@ def load() -> ctypes.CDLL:
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, u32] + [vp] * 10 + [vp]
     lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ssm_shape)]
+    lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_bwd.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 21 + [ctypes.c_size_t, vp]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 6 + [vp]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
     lib.ssm_conv1d_update.argtypes = [i64, i64, i64, i32] + [vp] * 5 + [vp]
@@ -185,6 +189,54 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
                                 _stream(stream)))
     return out
+
+
+def bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SSM_BF16, reverse=False) -> int:
+    sh = make_shape(batch, dim, dstate, seqlen, io_dtype, False, reverse)
+    return int(load().ssm_scan_bwd_workspace_size(ctypes.byref(sh)))
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *, dout,
+             dfinal_state=None, reverse=False, grads=None, workspace=None, stream=None):
+    """Gradients of scan_fwd for output gradient dout [B,D,L] (u's dtype) and optional
+    final-state gradient [B,D,N] fp32.  Returns a dict: du, ddelta (u's dtype), dA [D,N], dB, dC
+    [B,N,L], dD, ddelta_bias [D] (fp32), dz (u's dtype, None without z) and dinitial_state
+    [B,D,N] fp32.  grads: optional dict of preallocated outputs with those names."""
+    lib = load()
+    Bsz, Dm, L = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    sh = make_shape(Bsz, Dm, N, L, io, False, reverse)
+    f32, dev = torch.float32, u.device
+    for t, shp, dt, name in ((delta, (Bsz, Dm, L), u.dtype, "delta"), (A, (Dm, N), f32, "A"),
+                             (B, (Bsz, N, L), u.dtype, "B"), (C, (Bsz, N, L), u.dtype, "C"),
+                             (D, (Dm,), f32, "D"), (z, (Bsz, Dm, L), u.dtype, "z"),
+                             (delta_bias, (Dm,), f32, "delta_bias"),
+                             (initial_state, (Bsz, Dm, N), f32, "initial_state"),
+                             (dout, (Bsz, Dm, L), u.dtype, "dout"),
+                             (dfinal_state, (Bsz, Dm, N), f32, "dfinal_state")):
+        _expect(t, shp, dt, name)
+    shapes = dict(du=((Bsz, Dm, L), u.dtype), ddelta=((Bsz, Dm, L), u.dtype), dA=((Dm, N), f32),
+                  dB=((Bsz, N, L), f32), dC=((Bsz, N, L), f32), dD=((Dm,), f32),
+                  dz=((Bsz, Dm, L), u.dtype), ddelta_bias=((Dm,), f32), dinitial_state=((Bsz, Dm, N), f32))
+    g = dict(grads or {})
+    for k, (shp, dt) in shapes.items():
+        if k == "dz" and z is None:
+            g[k] = None
+            continue
+        if g.get(k) is None:
+            g[k] = torch.empty(shp, dtype=dt, device=dev)
+        _expect(g[k], shp, dt, k)
+    need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(sh)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.ssm_scan_bwd(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), _ptr(initial_state), _ptr(dout), _ptr(dfinal_state),
+                            _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                            _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]),
+                            _ptr(workspace), ws_bytes, _stream(stream)))
+    return g
 
 
 def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_state=True, stream=None):

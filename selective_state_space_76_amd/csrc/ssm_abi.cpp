@@ -82,6 +82,28 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
 
 ssm_status launch_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH; }
 
+struct BwdPlan {
+  int64_t nblk = 0, nbk = 0;
+  size_t ckpt = 0, bc = 0, a = 0, d = 0, total = 0;
+};
+
+bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl) {
+  Plan fp;
+  if (!make_plan(s, &fp)) return false;  // same size limits as the forward
+  const int64_t Bsz = s->batch, Dm = s->dim, N = s->dstate, L = s->seqlen;
+  pl->nblk = (Dm + 15) / 16;
+  pl->nbk = (L + 63) / 64;
+  int64_t x;
+  if (!mul_ok(Bsz * Dm * N, pl->nbk, &x)) return false;
+  pl->ckpt = round256(sizeof(float) * (size_t)x);
+  if (!mul_ok(2 * pl->nblk * Bsz * N, L, &x)) return false;
+  pl->bc = round256(sizeof(float) * (size_t)x);
+  pl->a = round256(sizeof(float) * (size_t)(Bsz * Dm * N));
+  pl->d = round256(sizeof(float) * (size_t)(2 * Bsz * Dm));
+  pl->total = pl->ckpt + pl->bc + pl->a + pl->d;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,6 +236,105 @@ ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t 
   p.vec = (dstate % 4) == 0 ? 1 : 0;
   p.zoh = (flags & SSM_FLAG_ZOH) ? 1 : 0;
   return launch_status(ssm::launch_step(p, io_dtype == SSM_BF16, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t ssm_scan_bwd_workspace_size(const ssm_shape* shape) {
+  BwdPlan pl;
+  if (!make_bwd_plan(shape, &pl)) return 0;
+  return pl.total;
+}
+
+ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, const float* initial_state, const void* dout,
+                        const float* dfinal_state, void* du, void* ddelta, float* dA, float* dB,
+                        float* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
+                        void* workspace, size_t workspace_bytes, struct ihipStream_t* stream) {
+  if (!shape) return SSM_ERR_NULL;
+  if (shape->io_dtype != SSM_F32 && shape->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (shape->flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE)) return SSM_ERR_UNSUPPORTED;
+  if (shape->flags & SSM_FLAG_ZOH) return SSM_ERR_UNSUPPORTED;
+  BwdPlan pl;
+  if (!make_bwd_plan(shape, &pl)) return SSM_ERR_SHAPE;
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC || !workspace)
+    return SSM_ERR_NULL;
+  if (z && !dz) return SSM_ERR_NULL;
+  if (!z) dz = nullptr;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, initial_state, dout, dfinal_state, du,
+                        ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return SSM_ERR_ALIGN;
+  if (workspace_bytes < pl.total) return SSM_ERR_WORKSPACE;
+
+  const int64_t Bsz = shape->batch, Dm = shape->dim, N = shape->dstate, L = shape->seqlen;
+  const int64_t es = shape->io_dtype == SSM_BF16 ? 2 : 4;
+  const int64_t BDL = Bsz * Dm * L, BNL = Bsz * N * L, BDN = Bsz * Dm * N;
+  const Range ins[] = {span(u, BDL, es), span(delta, BDL, es), span(A, Dm * N, 4), span(B, BNL, es),
+                       span(C, BNL, es), span(D, D ? Dm : 0, 4), span(z, z ? BDL : 0, es),
+                       span(delta_bias, delta_bias ? Dm : 0, 4),
+                       span(initial_state, initial_state ? BDN : 0, 4), span(dout, BDL, es),
+                       span(dfinal_state, dfinal_state ? BDN : 0, 4)};
+  const Range outs[] = {span(du, BDL, es), span(ddelta, BDL, es), span(dA, Dm * N, 4), span(dB, BNL, 4),
+                        span(dC, BNL, 4), span(dD, dD ? Dm : 0, 4), span(dz, dz ? BDL : 0, es),
+                        span(ddelta_bias, ddelta_bias ? Dm : 0, 4),
+                        span(dinitial_state, dinitial_state ? BDN : 0, 4),
+                        span(workspace, (int64_t)pl.total, 1)};
+  const size_t nin = sizeof(ins) / sizeof(ins[0]), nout = sizeof(outs) / sizeof(outs[0]);
+  for (size_t i = 0; i < nout; ++i) {
+    for (size_t j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return SSM_ERR_OVERLAP;
+    for (size_t j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j])) return SSM_ERR_OVERLAP;
+  }
+
+  const bool bf16 = shape->io_dtype == SSM_BF16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* ckpt = reinterpret_cast<float*>(ws);
+  float* part_bc = reinterpret_cast<float*>(ws + pl.ckpt);
+  float* part_a = reinterpret_cast<float*>(ws + pl.ckpt + pl.bc);
+  float* part_d = reinterpret_cast<float*>(ws + pl.ckpt + pl.bc + pl.a);
+  const int vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;
+  const int rev = (shape->flags & SSM_FLAG_REVERSE) ? 1 : 0;
+
+  ssm::ScanParams fp;
+  memset(&fp, 0, sizeof(fp));
+  fp.u = u; fp.delta = delta; fp.A = A; fp.B = B; fp.C = C; fp.bias = delta_bias; fp.init = initial_state;
+  fp.ckpt = ckpt;
+  fp.Bsz = Bsz; fp.Dm = Dm; fp.N = N; fp.L = L;
+  fp.S = 1;
+  fp.seg_len = pl.nbk * 64;
+  fp.nblk = (int)pl.nblk;
+  fp.vec = vec;
+  fp.reverse = rev;
+  ssm_status rc = launch_status(ssm::launch_ckpt(fp, bf16, st));
+  if (rc != SSM_OK) return rc;
+
+  ssm::BwdParams bp;
+  memset(&bp, 0, sizeof(bp));
+  bp.u = u; bp.delta = delta; bp.A = A; bp.B = B; bp.C = C; bp.D = D; bp.z = z; bp.bias = delta_bias;
+  bp.dout = dout; bp.dfinal = dfinal_state; bp.ckpt = ckpt;
+  bp.du = du; bp.ddelta = ddelta; bp.dz = dz; bp.dh0 = dinitial_state;
+  bp.part_bc = part_bc; bp.part_a = part_a; bp.part_d = part_d;
+  bp.Bsz = Bsz; bp.Dm = Dm; bp.N = N; bp.L = L;
+  bp.nblk = (int)pl.nblk;
+  bp.vec = vec;
+  bp.reverse = rev;
+  rc = launch_status(ssm::launch_bwd(bp, bf16, st));
+  if (rc != SSM_OK) return rc;
+
+  rc = launch_status(ssm::launch_reduce(dB, part_bc, pl.nblk, BNL, BNL, st));
+  if (rc != SSM_OK) return rc;
+  rc = launch_status(ssm::launch_reduce(dC, part_bc + pl.nblk * BNL, pl.nblk, BNL, BNL, st));
+  if (rc != SSM_OK) return rc;
+  rc = launch_status(ssm::launch_reduce(dA, part_a, Bsz, Dm * N, Dm * N, st));
+  if (rc != SSM_OK) return rc;
+  if (dD) {
+    rc = launch_status(ssm::launch_reduce(dD, part_d, Bsz, Dm, Dm, st));
+    if (rc != SSM_OK) return rc;
+  }
+  if (ddelta_bias) rc = launch_status(ssm::launch_reduce(ddelta_bias, part_d + Bsz * Dm, Bsz, Dm, Dm, st));
+  return rc;
 }
 
 ssm_status ssm_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int32_t io_dtype,

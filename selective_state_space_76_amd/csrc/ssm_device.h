@@ -175,6 +175,8 @@ __device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
 
 // MODE 0: output pass (writes out and, for the last segment, final_state).
 // MODE 1: summary pass over segments 0..S-2 (writes seg_state and seg_dsum).
+// MODE 2: checkpoint pass for the backward (one segment; writes the state
+//         entering every 64-step block to ckpt).
 // REV: logical step t reads physical position L-1-t.  VEC: rows allow 16-byte
 // vector loads (L a multiple of 8 for bf16, of 4 for fp32, and L >= 8).
 //
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int r = lane >> 4, g = lane & 15;
-  const int S_launch = MODE == 0 ? p.S : p.S - 1;
+  const int S_launch = MODE == 1 ? p.S - 1 : p.S;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int cb = logical % p.nblk;
   const int rest = logical / p.nblk;
@@ -228,8 +230,8 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
     Aln[i] = nv ? a : 0.0f;
     Ap[i] = Aln[i] * kLog2e;
     float h0 = 0.0f;
-    if (MODE == 0) {
-      if (p.carries) h0 = p.carries[(((int64_t)seg * p.Bsz + b) * Dm + dd) * N + nn];
+    if (MODE != 1) {
+      if (MODE == 0 && p.carries) h0 = p.carries[(((int64_t)seg * p.Bsz + b) * Dm + dd) * N + nn];
       else if (p.init) h0 = p.init[(b * Dm + dd) * N + nn];
     }
     h[i] = nv ? h0 : 0.0f;
@@ -342,6 +344,12 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
       if (t0 + 64 < te) fetch(t0 + 64);  // next block streams in while this one is computed
       __syncthreads();  // tile visible
     }
+    if (MODE == 2 && dval) {
+      const int64_t nbk = (L + 63) / 64;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (g + 16 * i < N) p.ckpt[((b * nbk + blk) * Dm + d) * N + g + 16 * i] = h[i];
+    }
     const float* Bt = tile;
     const float* Ct = tile + (MODE == 0 ? NP * TS : 0);
     const float* dch = tile + NT * NP * TS + cl * TS;          // this channel's delta row
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
       for (int i = 0; i < NL; ++i)
         if (g + 16 * i < N) p.final_state[(b * Dm + d) * N + g + 16 * i] = h[i];
     }
-  } else {
+  } else if (MODE == 1) {
     // row sum of the lanes' step-size sums
     float ds = dsum;
 #pragma unroll

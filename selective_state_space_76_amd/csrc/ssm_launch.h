@@ -19,6 +19,7 @@ struct ScanParams {
   float* carries;        // [S,B,D,N] state entering each segment (split runs), or null
   void* out;
   float* final_state;
+  float* ckpt;           // [B,nb,D,N] state entering each 64-step block (checkpoint pass), or null
   float* seg_state;      // [S-1,B,D,N] end state of each segment scanned from zero
   float* seg_dsum;       // [S-1,B,D] sum of the step sizes of each segment
   int64_t Bsz, Dm, N, L;
@@ -46,6 +47,31 @@ struct StepParams {
   int zoh;
 };
 
+struct BwdParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const void* dout;       // [B,D,L] gradient of out
+  const float* dfinal;    // [B,D,N] gradient of final_state, or null
+  const float* ckpt;      // [B,nb,D,N] state entering each 64-step block
+  void* du;               // [B,D,L]
+  void* ddelta;           // [B,D,L]
+  void* dz;               // [B,D,L], written when z is given
+  float* dh0;             // [B,D,N] gradient of the initial state, or null
+  float* part_bc;         // [2,nblk,B,N,L] dB and dC summed over each workgroup's 16 channels
+  float* part_a;          // [B,D,N] dA summed over steps, per batch row
+  float* part_d;          // [2,B,D] dD and dbias summed over steps, per batch row
+  int64_t Bsz, Dm, N, L;
+  int nblk;               // channel blocks of 16
+  int vec;                // rows allow 16-byte vector loads
+  int reverse;
+};
+
 struct ConvParams {
   const void* x;          // [B,D,L] (decode: [B,D])
   const float* w;         // [D,K]
@@ -61,6 +87,11 @@ hipError_t launch_scan(const ScanParams& p, bool bf16, int mode, hipStream_t s);
 // mode 0: per-element prefill, 1: 16-byte-chunk prefill (L a multiple of the chunk), 2: decode step
 hipError_t launch_conv(const ConvParams& p, bool bf16, int mode, hipStream_t s);
 hipError_t launch_carry(const ScanParams& p, hipStream_t s);
+// checkpoint pass (the scan kernel's mode 2), backward pass, and the fixed-order partial sums
+hipError_t launch_ckpt(const ScanParams& p, bool bf16, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
+// out[i] = sum_k part[k * stride + i] for i < n, k < count (k ascending)
+hipError_t launch_reduce(float* out, const float* part, int64_t count, int64_t stride, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
 
 }  // namespace ssm

@@ -174,3 +174,40 @@ def test_conv_update_errors():
     assert conv_upd(u=fake(2, off=16)) == 8      # u inside x
     assert conv_upd(st=fake(3)) == 8             # state over the weights
     assert conv_upd(u=fake(1, off=16)) == 8      # u inside the state
+
+
+def bwd(shape, ws_bytes=None, **kw):
+    lib = L.load()
+    names = ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0", "dout", "dfin", "du", "ddelta", "dA", "dB",
+             "dC", "dD", "dz", "dbias", "dh0", "ws"]
+    p = dict(u=fake(1), delta=fake(2), A=fake(3), B=fake(4), C=fake(5), dout=fake(6), du=fake(7), ddelta=fake(8),
+             dA=fake(9), dB=fake(10), dC=fake(11), ws=fake(12))
+    p.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.ssm_scan_bwd_workspace_size(ctypes.byref(shape)) if shape is not None else 0
+    return lib.ssm_scan_bwd(None if shape is None else ctypes.byref(shape), *[p.get(n) for n in names],
+                            ws_bytes, None)
+
+
+def test_bwd_errors():
+    lib = L.load()
+    s = shp()
+    need = lib.ssm_scan_bwd_workspace_size(ctypes.byref(s))
+    nblk, nbk = (64 + 15) // 16, (128 + 63) // 64
+    r = lambda x: (x + 255) // 256 * 256
+    assert need == (r(4 * 2 * 64 * 16 * nbk) + r(4 * 2 * nblk * 2 * 16 * 128) + r(4 * 2 * 64 * 16)
+                    + r(4 * 2 * 2 * 64))
+    assert bwd(None) == 1
+    for name in ("u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA", "dB", "dC", "ws"):
+        assert bwd(shp(), **{name: None}) == 1, name
+    assert bwd(shp(), z=fake(13)) == 1                      # z given without dz
+    assert bwd(shp(flags=L.SSM_FLAG_ZOH)) == 5              # ZOH gradients are not provided
+    assert bwd(shp(flags=8)) == 5
+    assert bwd(shp(io_dtype=3)) == 3
+    assert bwd(shp(dstate=65)) == 2
+    assert bwd(shp(), ws_bytes=need - 1) == 6
+    assert bwd(shp(), dB=fake(10, off=4)) == 4
+    assert bwd(shp(), du=fake(1, off=64)) == 8              # output inside an input
+    assert bwd(shp(), dC=fake(10, off=256)) == 8            # two outputs overlap
+    assert bwd(shp(), ws=fake(9)) == 8                      # workspace over an output
+    assert bwd(shp(flags=L.SSM_FLAG_REVERSE), du=fake(1, off=64)) == 8
