@@ -8,7 +8,8 @@ scan, carry, output epilogue: the entire prefill/training-forward path) with
 every input already resident in HBM.  The timed loop rotates through enough
 independent input sets that they cannot be served from the 256 MB Infinity
 Cache.  The same JSON line also carries the decode path (ssm_state_update) on
-the 2.8B-shaped generation workload, the conv + SiLU step that produces u
+the 2.8B-shaped generation workload, the backward pass (ssm_scan_bwd) on the
+same workload, the conv + SiLU step that produces u
 (ssm_conv1d_fwd on the same [B, D, L] shape, ssm_conv1d_update on the decode
 shape) and the fp64 CPU oracle's rate on the host.
 
@@ -160,6 +161,57 @@ def bench_decode(args, torch, ssm, W):
     }
 
 
+def bwd_bytes(w) -> int:
+    """Algorithmic HBM bytes of one backward call: the forward's inputs and dout read once,
+    du, ddelta and dz written once, dB, dC (fp32) and the per-channel gradients written once."""
+    s = 4 if w.io == "f32" else 2
+    BDL, BNL = w.batch * w.dim * w.seqlen, w.batch * w.dstate * w.seqlen
+    return (4 * s * BDL + 2 * s * BNL + 3 * s * BDL + 2 * 4 * BNL + 2 * 4 * w.dim * w.dstate
+            + 4 * 4 * w.dim)
+
+
+def bench_bwd(args, torch, ssm, W):
+    """One ssm_scan_bwd call per step on the scan workload (checkpoint pass, backward pass and
+    the fixed-order partial sums), inputs rotated past the Infinity Cache."""
+    w = W.WORKLOADS[args.workload]
+    per_set = bwd_bytes(w)
+    R = max(1, min(4, math.ceil(2 * MALL_BYTES / per_set)))
+    sets = []
+    for k in range(R):
+        x = W.scan_inputs(w.with_shape(seed=w.seed + 1000 * k), device="cuda")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed + 77 + k)
+        x["dout"] = torch.randn(w.batch, w.dim, w.seqlen, generator=g, device="cuda").to(x["u"].dtype)
+        sets.append(x)
+    need = ssm.bwd_workspace_size(w.batch, w.dim, w.dstate, w.seqlen,
+                                  ssm.SSM_BF16 if w.io == "bf16" else ssm.SSM_F32)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    grads = None
+
+    def call(x):
+        nonlocal grads
+        grads = ssm.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                             dout=x["dout"], grads=grads, workspace=ws)
+
+    for k in range(max(2, args.warmup)):
+        call(sets[k % R])
+    n = max(5, args.steps // 2)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        ev[2 * k].record()
+        call(sets[k % R])
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n))
+    mean = sum(ms) / n
+    b = bwd_bytes(w)
+    return {"workload": w.name, "rotated_input_sets": R, "call_ms": mean, "call_ms_median": ms[n // 2],
+            "value": w.updates / (mean * 1e-3), "unit": "state-updates/s",
+            "workspace_bytes": need, "algorithmic_bytes_per_call": b,
+            "hbm_GBs": b / (mean * 1e-3) / 1e9}
+
+
 def conv_bytes(w, K) -> int:
     """Algorithmic HBM bytes of one conv prefill call: x read, u written, the carried-out state
     written, weights and bias read."""
@@ -290,6 +342,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -346,6 +399,10 @@ def main():
         log("decode: %.4f ms/step wall, %.4f ms/step events, %.1f GB/s" % (d["ms_per_step"], d["gpu_ms_per_step"],
                                                                           d["roofline"]["achieved"]))
         res["decode"] = d
+    if not args.no_bwd:
+        bw = bench_bwd(args, torch, ssm, W)
+        log("backward: %.4f ms/call -> %.3e updates/s" % (bw["call_ms"], bw["value"]))
+        res["backward"] = bw
     if not args.no_conv:
         pre, dec = bench_conv(args, torch, ssm, W)
         log("conv1d: %.4f ms/launch, %.1f GB/s; conv1d_update: %.4f ms/step, %.1f GB/s"

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_kernel(BwdParams p) {
   constexpr int CPT = (NCH + 255) / 256;
   constexpr int TILE = NT * NP * TS + NS * 16 * TS;
   constexpr int RED = 4 * 2 * 16 * NP;         // per-wave dB/dC sums of one sub-block
-  constexpr bool KEEP_A = NL == 1;             // keep the decay factors of a sub-block in registers
+  constexpr bool KEEP_A = NL == 1;             // keep a sub-block's states and decay factors from the y pass
   __shared__ __attribute__((aligned(16))) float tiles[TILE];
   __shared__ float red[2 * RED];               // double-buffered by sub-block parity
 
@@ -232,9 +232,10 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_kernel(BwdParams p) {
     float dug[4], ddg[4], dzg[4];
 #pragma unroll
     for (int s = 3; s >= 0; --s) {
-      // forward through the sub-block: the states after each step and y
-      float hv[NL][16];
-      float av[KEEP_A ? NL : 1][16];
+      // forward through the sub-block for y.  With one state slice (NL == 1) the states and
+      // decay factors are kept for the backward sweep; with more, each slice is recomputed
+      // right before its backward sweep so only one slice is ever held in registers.
+      float hv[16], av[16];
       float pj[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) pj[j] = 0.0f;
@@ -246,9 +247,11 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_kernel(BwdParams p) {
         static_for<0, 16>([&](auto j_) {
           constexpr int j = decltype(j_)::value;
           const float a = exp2_(row_bcast<j>(dt[s]) * Ap[i]);
-          if constexpr (KEEP_A) av[i][j] = a;
           h = __builtin_fmaf(a, h, row_bcast<j>(xu[s]) * brow[j]);
-          hv[i][j] = h;
+          if constexpr (KEEP_A) {
+            av[j] = a;
+            hv[j] = h;
+          }
           pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
         });
       }
@@ -270,18 +273,26 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_kernel(BwdParams p) {
       for (int i = 0; i < NL; ++i) {
         const float* brow = Bt + (g + 16 * i) * TS + 16 * s;
         const float* crow = Ct + (g + 16 * i) * TS + 16 * s;
+        if constexpr (!KEEP_A) {
+          float h = hs[s][i];
+          static_for<0, 16>([&](auto j_) {
+            constexpr int j = decltype(j_)::value;
+            const float a = exp2_(row_bcast<j>(dt[s]) * Ap[i]);
+            h = __builtin_fmaf(a, h, row_bcast<j>(xu[s]) * brow[j]);
+            av[j] = a;
+            hv[j] = h;
+          });
+        }
         float Gi = G[i], dAi = dAacc[i];
         float xo = 0.0f, yo = 0.0f;  // dB, dC contributions of the odd step of a pair
         static_for<0, 16>([&](auto k_) {
           constexpr int j = 15 - decltype(k_)::value;
           const float dyj = row_bcast<j>(dy);
           Gi = __builtin_fmaf(dyj, crow[j], Gi);
-          const float yc = dyj * hv[i][j];
+          const float yc = dyj * hv[j];
           s1[j] = __builtin_fmaf(Gi, brow[j], s1[j]);
-          float a;
-          if constexpr (KEEP_A) a = av[i][j];
-          else a = exp2_(row_bcast<j>(dt[s]) * Ap[i]);
-          const float hp = j > 0 ? hv[i][j > 0 ? j - 1 : 0] : hs[s][i];
+          const float a = av[j];
+          const float hp = j > 0 ? hv[j > 0 ? j - 1 : 0] : hs[s][i];
           const float tt = Gi * hp * a;
           s2[j] = __builtin_fmaf(tt, Aln[i], s2[j]);
           dAi = __builtin_fmaf(tt, row_bcast<j>(dt[s]), dAi);
@@ -361,13 +372,44 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_kernel(BwdParams p) {
   }
 }
 
+// out[i] = sum over k of part[k * stride + i], k ascending (the same order on every run).
+// V4: 4 consecutive outputs per lane with 16-byte loads (stride and n multiples of 4); the
+// loads of 8 consecutive k are issued before their adds, which keep the k order.
+template <bool V4>
 __global__ __launch_bounds__(256) void reduce_kernel(float* out, const float* part, int64_t count,
                                                      int64_t stride, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int W = V4 ? 4 : 1;
+  constexpr int U = 8;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * W;
   if (i >= n) return;
-  float s = 0.0f;
-  for (int64_t k = 0; k < count; ++k) s += part[k * stride + i];
-  out[i] = s;
+  float acc[W];
+#pragma unroll
+  for (int e = 0; e < W; ++e) acc[e] = 0.0f;
+  int64_t k = 0;
+  for (; k + U <= count; k += U) {
+    float v[U][W];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* q = part + (k + u) * stride + i;
+      if constexpr (V4) {
+        const float4 t = *reinterpret_cast<const float4*>(q);
+        v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
+      } else {
+        v[u][0] = *q;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < W; ++e) acc[e] += v[u][e];
+  }
+  for (; k < count; ++k) {
+    const float* q = part + k * stride + i;
+#pragma unroll
+    for (int e = 0; e < W; ++e) acc[e] += q[e];
+  }
+  if constexpr (V4) *reinterpret_cast<float4*>(out + i) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  else out[i] = acc[0];
 }
 
 namespace {
@@ -433,7 +475,15 @@ hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_reduce(float* out, const float* part, int64_t count, int64_t stride, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, part, count, stride, n);
+  // 16-byte path when every row start stays 16-byte aligned (bases are 16-byte aligned)
+  if (stride % 4 == 0 && n % 4 == 0) {
+    const int64_t lanes = n / 4;
+    hipLaunchKernelGGL((reduce_kernel<true>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, out, part,
+                       count, stride, n);
+  } else {
+    hipLaunchKernelGGL((reduce_kernel<false>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, part,
+                       count, stride, n);
+  }
   return hipGetLastError();
 }
 
