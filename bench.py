@@ -303,7 +303,8 @@ def bench_conv(args, torch, ssm, W, K=4):
            "rotated_state_buffers": nstate, "gpu_ms_per_step": gpu_ms, "timing": "HIP graph of the steps, replayed",
            "eager_ms_per_step": eager_ms,
            "roofline": {"bound": "hbm", "achieved": bd / (gpu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": bd / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                        "frac": bd / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "traffic": traffic_from_profile("conv_update_" + wd.name, 1),
                         "algorithmic_bytes_per_step": bd}}
     return pre, dec
 
