@@ -184,7 +184,7 @@ __device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
 // states (rows >= N stay zero) and delta/u/z of its 16 channels, all fetched
 // with coalesced 16-byte loads one block ahead into registers.
 template <typename IO, int NL, int MODE, bool ZOH, bool REV, bool VEC>
-__global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2) void scan_kernel(ScanParams p) {
   constexpr int NP = 16 * NL;                  // states padded to the lane grid
   constexpr int TS = 68;                       // LDS tile row: 64 steps + 4 pad (floats)
   constexpr int NT = MODE == 0 ? 2 : 1;        // staged coefficient tensors: B and C, or B only
@@ -194,7 +194,10 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? 3 : 2) : 2) void scan_k
   constexpr int NBC = NT * NP * CPR;           // coefficient chunks
   constexpr int NCH = NBC + NS * 16 * CPR;     // + channel-stream chunks
   constexpr int CPT = (NCH + 255) / 256;       // chunks per thread
-  constexpr int NBUF = NL == 1 ? 2 : 1;        // double-buffered tiles when LDS allows (one barrier per block)
+  // One state per lane: single-buffered tiles (21.8 KB) so 4 workgroups fit a CU -- a fourth wave per
+  // SIMD measured faster than double buffering with 3.  The ZOH variant needs more registers than 4
+  // waves allow, so it keeps 3 waves and double-buffered tiles (one barrier per block).
+  constexpr int NBUF = (NL == 1 && ZOH) ? 2 : 1;
   constexpr int TILE = NT * NP * TS + NS * 16 * TS;
   __shared__ __attribute__((aligned(16))) float tiles[NBUF * TILE];
 
