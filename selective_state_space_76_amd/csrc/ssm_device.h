@@ -561,4 +561,91 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   }
 }
 
+// Decode step when N is a multiple of 4: G lanes per channel (G >= N/4, a power of two) with 4
+// states each, and U channel slots per thread.  Every slot's loads (the state with a nontemporal
+// 16-byte access, A, B, C and the channel's delta/u/z) are issued before any arithmetic, so each lane
+// keeps U x 16 bytes of state in flight; slot k of a workgroup lies 256 lanes after slot k-1, so every
+// load instruction still covers contiguous memory.
+template <typename IO, int G, int U, bool ZOH>
+__global__ __launch_bounds__(256) void step4_kernel(StepParams p) {
+  const int64_t BD = p.Bsz * p.Dm;
+  const int64_t N = p.N;
+  // Loads are unconditional, from addresses clamped into range, so all slots' loads issue back to
+  // back; lanes past the last channel or the last state quad are masked out by selects and by the
+  // guarded stores.
+  f32x4 hq[U];
+  float4 aq[U];
+  float Bv[U][4], Cv[U][4];
+  float dlv[U], uvv[U], zvv[U], bsv[U], dsv[U];
+  int64_t ccs[U], n0s[U];
+  int qs[U];
+  bool cvs[U], lv[U];
+  const void* zsrc = p.z ? p.z : p.u;  // without a gate the loaded value is unused
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t gid = ((int64_t)blockIdx.x * U + k) * 256 + threadIdx.x;
+    const int64_t c = gid / G;
+    const int q = (int)(gid % G);
+    const bool cval = c < BD;
+    const int64_t cc = cval ? c : BD - 1;
+    const int64_t b = cc / p.Dm, d = cc - b * p.Dm;
+    const int64_t n0 = 4 * (int64_t)q;
+    const bool live = cval && n0 < N;
+    const int64_t nc = n0 < N ? n0 : 0;
+    ccs[k] = cc; n0s[k] = nc; qs[k] = q; cvs[k] = cval; lv[k] = live;
+    hq[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.state + cc * N + nc));
+    aq[k] = *reinterpret_cast<const float4*>(p.A + d * N + nc);
+    const IO* Bp = reinterpret_cast<const IO*>(p.B) + b * N + nc;
+    const IO* Cp = reinterpret_cast<const IO*>(p.C) + b * N + nc;
+    if constexpr (sizeof(IO) == 2) {  // 4 bf16 states = one 8-byte load each
+      const uint2 bq = *reinterpret_cast<const uint2*>(Bp);
+      const uint2 cq = *reinterpret_cast<const uint2*>(Cp);
+      Bv[k][0] = __uint_as_float(bq.x << 16); Bv[k][1] = __uint_as_float(bq.x & 0xffff0000u);
+      Bv[k][2] = __uint_as_float(bq.y << 16); Bv[k][3] = __uint_as_float(bq.y & 0xffff0000u);
+      Cv[k][0] = __uint_as_float(cq.x << 16); Cv[k][1] = __uint_as_float(cq.x & 0xffff0000u);
+      Cv[k][2] = __uint_as_float(cq.y << 16); Cv[k][3] = __uint_as_float(cq.y & 0xffff0000u);
+    } else {
+      const float4 bq = *reinterpret_cast<const float4*>(Bp);
+      const float4 cq = *reinterpret_cast<const float4*>(Cp);
+      Bv[k][0] = bq.x; Bv[k][1] = bq.y; Bv[k][2] = bq.z; Bv[k][3] = bq.w;
+      Cv[k][0] = cq.x; Cv[k][1] = cq.y; Cv[k][2] = cq.z; Cv[k][3] = cq.w;
+    }
+    dlv[k] = to_f32(reinterpret_cast<const IO*>(p.delta)[cc]);
+    uvv[k] = to_f32(reinterpret_cast<const IO*>(p.u)[cc]);
+    zvv[k] = to_f32(reinterpret_cast<const IO*>(zsrc)[cc]);
+    bsv[k] = p.bias ? p.bias[d] : 0.0f;
+    dsv[k] = p.D ? p.D[d] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int64_t cc = ccs[k];
+    const float dt = softplus_(dlv[k] + bsv[k]);
+    const float xu = ZOH ? uvv[k] : dt * uvv[k];
+    const float hv[4] = {hq[k].x, hq[k].y, hq[k].z, hq[k].w};
+    const float Av[4] = {aq[k].x, aq[k].y, aq[k].z, aq[k].w};
+    float hn[4];
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = exp2_(dt * Av[e] * kLog2e);
+      float x;
+      if (ZOH) x = (dt * expm1_over_x(dt * Av[e], a)) * (xu * Bv[k][e]);
+      else x = xu * Bv[k][e];
+      hn[e] = __builtin_fmaf(a, hv[e], x);
+      acc = __builtin_fmaf(lv[k] ? Cv[k][e] : 0.0f, hn[e], acc);  // padding quads add nothing
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, G);
+    if (cvs[k] && qs[k] == 0) {
+      float y = acc + dsv[k] * uvv[k];
+      if (p.z) y *= silu_(zvv[k]);
+      store_io(reinterpret_cast<IO*>(p.out) + cc, y);
+    }
+    if (lv[k]) {
+      const f32x4 o = {hn[0], hn[1], hn[2], hn[3]};
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(p.state + cc * N + n0s[k]));
+    }
+  }
+}
+
 }  // namespace ssm
