@@ -335,6 +335,35 @@ def bench_conv(args, torch, ssm, W, K=4):
     return pre, dec
 
 
+def copy_peak(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate (torch copy_ of nbytes): read + write bytes per second."""
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(torch, x, w, seconds):
     """The fp64 oracle as it stands, on this host's cores, over the same inputs (repeated to ~seconds)."""
     sys.path.insert(0, ROOT)
@@ -356,6 +385,7 @@ def cpu_baseline(torch, x, w, seconds):
             break
     dt = time.perf_counter() - t0
     return {"value": upd / dt, "unit": "state-updates/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d full pass(es) of the %s workload (%d x %d x %d x %d, the same bf16 inputs widened "
                       "to fp64), %.1f s wall" % (runs, w.name, B_rows, w.dim, w.dstate, w.seqlen, dt)}
 
@@ -421,11 +451,16 @@ def main():
                 "algorithmic_bytes_per_launch": b},
         "kernel_source_hash": kernel_source_hash(),
     }
+    cp = copy_peak(torch)
+    res["hbm"]["copy_peak_GBs"] = cp
+    res["hbm"]["frac_of_copy_peak"] = gbs / cp
+    log("device copy (torch copy_, 1 GiB): %.1f GB/s" % cp)
     if not args.no_decode:
         d = bench_decode(args, torch, ssm, W)
         log("decode: %.4f ms/step eager wall, %.4f ms/step eager events, %.4f ms/step graph, %.1f GB/s"
             % (d["eager_wall_ms_per_step"], d["eager_gpu_ms_per_step"], d["gpu_ms_per_step"], d["roofline"]["achieved"]))
         res["decode"] = d
+        d["roofline"]["frac_of_copy_peak"] = d["roofline"]["achieved"] / cp
     if not args.no_bwd:
         bw = bench_bwd(args, torch, ssm, W)
         log("backward: %.4f ms/call -> %.3e updates/s" % (bw["call_ms"], bw["value"]))
@@ -434,6 +469,8 @@ def main():
         pre, dec = bench_conv(args, torch, ssm, W)
         log("conv1d: %.4f ms/launch, %.1f GB/s; conv1d_update: %.4f ms/step, %.1f GB/s"
             % (pre["launch_ms"], pre["roofline"]["achieved"], dec["gpu_ms_per_step"], dec["roofline"]["achieved"]))
+        pre["roofline"]["frac_of_copy_peak"] = pre["roofline"]["achieved"] / cp
+        dec["roofline"]["frac_of_copy_peak"] = dec["roofline"]["achieved"] / cp
         res["conv1d"] = pre
         res["conv1d_update"] = dec
     if not args.no_cpu_baseline:
