@@ -98,20 +98,23 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _expect(t, shape, dtype, name):
-    """The C ABI trusts sizes and element types; check them here so a mismatched tensor
-    is an error, not an out-of-bounds read."""
+def _expect(t, shape, dtype, name, device=None):
+    """The C ABI trusts sizes, element types and the device; check them here so a mismatched
+    tensor is an error, not an out-of-bounds read."""
     if t is None:
         return
     if tuple(t.shape) != tuple(shape):
         raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
     if t.dtype != dtype:
         raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s: expected a tensor on %s, got %s" % (name, device, t.device))
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The caller's stream, by default the current stream of the tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -138,6 +141,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     Bsz, Dm, L = u.shape
     N = A.shape[1]
     io = _io_dtype(u)
+    device = u.device
     sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
     if out is None:
         out = torch.empty_like(u)
@@ -153,8 +157,10 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                              (initial_state, (Bsz, Dm, N), f32, "initial_state"),
                              (out, (Bsz, Dm, L), u.dtype, "out"),
                              (final_state, (Bsz, Dm, N), f32, "final_state")):
-        _expect(t, shp, dt, name)
+        _expect(t, shp, dt, name, device)
     ws_bytes = 0
+    if workspace is not None and workspace.device != device:
+        raise ValueError("workspace: expected a tensor on %s, got %s" % (device, workspace.device))
     if split:
         need = int(lib.ssm_scan_workspace_size(ctypes.byref(sh)))
         if need and workspace is None:
@@ -165,7 +171,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
         workspace = None
     _check(lib.ssm_scan_fwd(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
-                            _ptr(workspace), ws_bytes, _stream(stream)))
+                            _ptr(workspace), ws_bytes, _stream(stream, device)))
     return out, final_state
 
 
@@ -177,6 +183,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     Bsz, Dm = u.shape
     N = A.shape[1]
     io = _io_dtype(u)
+    device = u.device
     if out is None:
         out = torch.empty_like(u)
     f32 = torch.float32
@@ -184,10 +191,10 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
                              (A, (Dm, N), f32, "A"), (B, (Bsz, N), u.dtype, "B"), (C, (Bsz, N), u.dtype, "C"),
                              (D, (Dm,), f32, "D"), (z, (Bsz, Dm), u.dtype, "z"),
                              (delta_bias, (Dm,), f32, "delta_bias"), (out, (Bsz, Dm), u.dtype, "out")):
-        _expect(t, shp, dt, name)
+        _expect(t, shp, dt, name, device)
     _check(lib.ssm_state_update(Bsz, Dm, N, io, SSM_FLAG_ZOH if zoh else 0, _ptr(state), _ptr(u), _ptr(delta),
                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
-                                _stream(stream)))
+                                _stream(stream, device)))
     return out
 
 
@@ -206,6 +213,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     Bsz, Dm, L = u.shape
     N = A.shape[1]
     io = _io_dtype(u)
+    device = u.device
     sh = make_shape(Bsz, Dm, N, L, io, False, reverse)
     f32, dev = torch.float32, u.device
     for t, shp, dt, name in ((delta, (Bsz, Dm, L), u.dtype, "delta"), (A, (Dm, N), f32, "A"),
@@ -215,7 +223,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                              (initial_state, (Bsz, Dm, N), f32, "initial_state"),
                              (dout, (Bsz, Dm, L), u.dtype, "dout"),
                              (dfinal_state, (Bsz, Dm, N), f32, "dfinal_state")):
-        _expect(t, shp, dt, name)
+        _expect(t, shp, dt, name, device)
     shapes = dict(du=((Bsz, Dm, L), u.dtype), ddelta=((Bsz, Dm, L), u.dtype), dA=((Dm, N), f32),
                   dB=((Bsz, N, L), f32), dC=((Bsz, N, L), f32), dD=((Dm,), f32),
                   dz=((Bsz, Dm, L), u.dtype), ddelta_bias=((Dm,), f32), dinitial_state=((Bsz, Dm, N), f32))
@@ -226,8 +234,10 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
             continue
         if g.get(k) is None:
             g[k] = torch.empty(shp, dtype=dt, device=dev)
-        _expect(g[k], shp, dt, k)
+        _expect(g[k], shp, dt, k, device)
     need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(sh)))
+    if workspace is not None and workspace.device != device:
+        raise ValueError("workspace: expected a tensor on %s, got %s" % (device, workspace.device))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -235,7 +245,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                             _ptr(delta_bias), _ptr(initial_state), _ptr(dout), _ptr(dfinal_state),
                             _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
                             _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]),
-                            _ptr(workspace), ws_bytes, _stream(stream)))
+                            _ptr(workspace), ws_bytes, _stream(stream, device)))
     return g
 
 
@@ -248,6 +258,7 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_stat
     Bsz, Dm, L = x.shape
     K = weight.shape[1]
     io = _io_dtype(x)
+    device = x.device
     if out is None:
         out = torch.empty_like(x)
     if final_state is True:
@@ -259,9 +270,9 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_stat
                              (initial_state, (Bsz, Dm, K - 1), x.dtype, "initial_state"),
                              (out, (Bsz, Dm, L), x.dtype, "out"),
                              (final_state, (Bsz, Dm, K - 1), x.dtype, "final_state")):
-        _expect(t, shp, dt, name)
+        _expect(t, shp, dt, name, device)
     _check(lib.ssm_conv1d_fwd(Bsz, Dm, L, K, io, _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state),
-                              _ptr(out), _ptr(final_state), _stream(stream)))
+                              _ptr(out), _ptr(final_state), _stream(stream, device)))
     return out, final_state
 
 
@@ -272,13 +283,14 @@ def conv1d_update(conv_state, x, weight, bias=None, *, out=None, stream=None):
     Bsz, Dm = x.shape
     K = weight.shape[1]
     io = _io_dtype(x)
+    device = x.device
     if out is None:
         out = torch.empty_like(x)
     f32 = torch.float32
     for t, shp, dt, name in ((conv_state, (Bsz, Dm, K - 1), x.dtype, "conv_state"),
                              (weight, (Dm, K), f32, "weight"), (bias, (Dm,), f32, "bias"),
                              (out, (Bsz, Dm), x.dtype, "out")):
-        _expect(t, shp, dt, name)
+        _expect(t, shp, dt, name, device)
     _check(lib.ssm_conv1d_update(Bsz, Dm, K, io, _ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias),
-                                 _ptr(out), _stream(stream)))
+                                 _ptr(out), _stream(stream, device)))
     return out
