@@ -4,7 +4,10 @@ Every gradient (du, ddelta, dA, dB, dC, dD, dz, ddelta_bias and the initial-stat
 gradient) is compared element by element on small shapes that span several
 64-step blocks, ragged tails, every states-per-lane variant, both dtypes, both
 scan directions and the optional operands; the 130M-class layer shape is
-compared in full.  Sums are taken in a fixed order, so two runs agree bit for bit."""
+compared in full, the 1.3B-class and million-step DNA shapes on sampled channels
+(the gradients that depend on their own channel only), and dB/dC at any size through
+their additivity over channel subsets.  Sums are taken in a fixed order, so two runs
+agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -105,3 +108,63 @@ def test_bwd_deterministic():
     for k in NAMES:
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
+
+
+def _sampled_channel_check(w, chans, dout_seed):
+    """Full backward on the GPU; the per-channel gradients (which depend on their own channel
+    only) compared with the oracle run on the sampled channels."""
+    x = W.scan_inputs(w, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(dout_seed)
+    dout = torch.randn(w.batch, w.dim, w.seqlen, generator=g, device=DEV).to(x["u"].dtype)
+    gr = scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], dout=dout)
+    torch.cuda.synchronize()
+    ci = torch.tensor(chans, device=DEV)
+    sel = lambda t: None if t is None else t.index_select(1, ci).cpu()
+    selc = lambda t: None if t is None else t.index_select(0, ci).cpu()
+    ref = oracle.scan_bwd(sel(x["u"]), sel(x["delta"]), selc(x["A"]), x["B"].cpu(), x["C"].cpu(), selc(x["D"]),
+                          sel(x["z"]), selc(x["delta_bias"]), dout=sel(dout))
+    got = {"du": sel(gr["du"]), "ddelta": sel(gr["ddelta"]), "dz": sel(gr["dz"]), "dA": selc(gr["dA"]),
+           "dD": selc(gr["dD"]), "ddelta_bias": selc(gr["ddelta_bias"]), "dh0": sel(gr["dinitial_state"])}
+    errs = {}
+    for k, v in got.items():
+        if v is None or ref[k] is None:
+            continue
+        errs[k] = rel_err(v, ref[k])
+    print("sampled rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()), flush=True)
+    bad = {k: e for k, e in errs.items() if not e <= tol_for(x["u"])}
+    assert not bad, bad
+
+
+def test_bwd_workload_mamba1p3b_sampled():
+    print("case: bwd 4x4096x64x4096 bf16, 6 channels compared", flush=True)
+    _sampled_channel_check(W.WORKLOADS["mamba1p3b"], [0, 1, 777, 2048, 4094, 4095], 8)
+
+
+def test_bwd_workload_dna1m_sampled():
+    print("case: bwd 1x1024x16x1048576 bf16, 4 channels compared", flush=True)
+    _sampled_channel_check(W.WORKLOADS["dna1m"], [0, 333, 512, 1023], 9)
+
+
+def test_bwd_dB_dC_add_over_channel_halves():
+    """dB and dC sum contributions over channels: the gradient over all channels equals the sum of
+    the gradients over the two halves of the channels (up to fp32 rounding of the sum)."""
+    x = make(3, 96, 16, 500, torch.float32, seed=21, h0=True, dfin=True)
+    full = run(x)
+    parts = []
+    for lo, hi in ((0, 48), (48, 96)):
+        h = {k: v for k, v in x.items()}
+        for k in ("u", "delta", "z", "dout"):
+            h[k] = x[k][:, lo:hi].contiguous()
+        for k in ("h0", "dfin"):
+            h[k] = x[k][:, lo:hi].contiguous()
+        for k in ("A",):
+            h[k] = x[k][lo:hi].contiguous()
+        for k in ("D", "delta_bias"):
+            h[k] = x[k][lo:hi].contiguous()
+        parts.append(run(h))
+    for k in ("dB", "dC"):
+        s = parts[0][k] + parts[1][k]
+        e = rel_err(full[k], s.double().cpu().numpy())
+        print("halves %s rel_err %.2g" % (k, e), flush=True)
+        assert e <= 1e-5, (k, e)
