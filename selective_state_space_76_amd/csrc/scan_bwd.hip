@@ -48,8 +48,10 @@ __device__ __forceinline__ float logistic_(float x) { return rcp_(1.0f + exp2_(-
 
 }  // namespace
 
+// With one state slice, three workgroups per CU (168 registers, a few spilled): the 130M-class
+// shape's 768 workgroups then run in one round instead of one and a half.
 template <typename IO, int NL, bool REV, bool VEC>
-__global__ __launch_bounds__(256, 2) void scan_bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, NL == 1 ? 3 : 2) void scan_bwd_kernel(BwdParams p) {
   constexpr int NP = 16 * NL;
   constexpr int TS = 68;                       // LDS tile row: 64 steps + 4 pad
   constexpr int NT = 2;                        // B, C
