@@ -172,6 +172,23 @@ def bench_decode(args, torch, ssm, W):
     torch.cuda.synchronize()
     gpu_ms = g0.elapsed_time(g1) / steps
     del graph
+    # the same steps on a single state buffer (84 MB, resident in the 256 MB Infinity Cache): the
+    # cache-warm rate, for comparison only
+    warm = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(warm, stream=side):
+        for k in range(steps):
+            x = inputs[k]
+            ssm.state_update(states[0], x["u"], x["delta"], A, x["B"], x["C"], Dv, x["z"], bias, out=outs[k % 2])
+    torch.cuda.current_stream().wait_stream(side)
+    warm.replay()
+    torch.cuda.synchronize()
+    g0.record()
+    warm.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    warm_ms = g0.elapsed_time(g1) / steps
+    del warm
     upd = w.batch * w.dim * w.dstate
     b = step_bytes(w)
     return {
@@ -179,6 +196,7 @@ def bench_decode(args, torch, ssm, W):
         "rotated_state_buffers": nstate,
         "value": upd / (gpu_ms * 1e-3), "unit": "state-updates/s", "eager_wall_ms_per_step": ms_step,
         "gpu_ms_per_step": gpu_ms, "timing": "HIP graph of the steps, replayed",
+        "mall_warm_gpu_ms_per_step": warm_ms,
         "eager_gpu_ms_per_step": eager_gpu_ms, "eager_median_step_ms": per[len(per) // 2],
         "eager_step_ms_from": "events every %d steps" % chunk,
         "roofline": {"bound": "hbm", "achieved": b / (gpu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -384,8 +402,13 @@ def cpu_baseline(torch, x, w, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": upd / dt, "unit": "state-updates/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "cpu_model": cpu_model(),
+    cores = oracle.max_threads()
+    t1 = time.perf_counter()
+    oracle.scan(host["u"], host["delta"], host["A"], host["B"], host["C"], D=host["D"], z=host["z"],
+                delta_bias=host["delta_bias"], threads=1)
+    one = w.batch * w.dim * w.dstate * w.seqlen / (time.perf_counter() - t1)
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "value_1_thread": one,
             "sample": "%d full pass(es) of the %s workload (%d x %d x %d x %d, the same bf16 inputs widened "
                       "to fp64), %.1f s wall" % (runs, w.name, B_rows, w.dim, w.dstate, w.seqlen, dt)}
 
@@ -446,10 +469,14 @@ def main():
         "roofline": {"bound": "alu", "achieved": alu, "peak": ALU_PEAK_TOPS, "unit": "T fp32-op/s",
                      "frac": alu / ALU_PEAK_TOPS, "traffic": traffic_from_profile(w.name, 1),
                      "ops_per_update": OPS_PER_UPDATE, "launch_ms": launch_ms,
-                     "launch_ms_median": all_launch[len(all_launch) // 2]},
+                     "launch_ms_median": all_launch[len(all_launch) // 2],
+                     "launch_ms_p10": all_launch[len(all_launch) // 10],
+                     "launch_ms_p90": all_launch[(9 * len(all_launch)) // 10]},
         "hbm": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                 "algorithmic_bytes_per_launch": b},
         "kernel_source_hash": kernel_source_hash(),
+        "input_fp64_sums": {k: float(v.double().sum()) for k, v in x0.items()
+                            if v is not None and k not in ("out", "fs")},
     }
     cp = copy_peak(torch)
     res["hbm"]["copy_peak_GBs"] = cp

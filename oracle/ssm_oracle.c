@@ -75,6 +75,10 @@ int oracle_max_threads(void) {
 #endif
 }
 
+/* Threads for one call: nthreads if positive, else the OpenMP default.  Passed to each parallel
+ * region, so a call never changes the count later calls use. */
+static int team_size(int nthreads) { return nthreads > 0 ? nthreads : oracle_max_threads(); }
+
 /* Returns 0 on success, -1 on bad arguments. nthreads <= 0 uses the OpenMP default. */
 int oracle_scan_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
                     const double* u, const double* delta, const double* A,
@@ -84,13 +88,10 @@ int oracle_scan_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
   if (Bsz < 0 || Dm < 0 || N <= 0 || L < 0) return -1;
   if (!u || !delta || !A || !Bm || !Cm || !out) return -1;
   const int64_t rows = Bsz * Dm;
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-  (void)nthreads;
-#endif
+  const int nt = team_size(nthreads);
+  (void)nt;  /* unused without OpenMP */
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
   for (int64_t r = 0; r < rows; ++r) {
     const int64_t b = r / Dm, d = r % Dm;
     double* h = (double*)malloc((size_t)N * sizeof(double));
@@ -138,12 +139,9 @@ int oracle_step_f64(int64_t Bsz, int64_t Dm, int64_t N, double* state,
   if (Bsz < 0 || Dm < 0 || N <= 0 || !state || !u || !delta || !A || !Bm || !Cm || !out)
     return -1;
   const int64_t rows = Bsz * Dm;
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-  (void)nthreads;
-#endif
-#pragma omp parallel for schedule(static)
+  const int nt = team_size(nthreads);
+  (void)nt;  /* unused without OpenMP */
+#pragma omp parallel for schedule(static) num_threads(nt)
   for (int64_t r = 0; r < rows; ++r) {
     const int64_t b = r / Dm, d = r % Dm;
     const double dt = softplus_f64(delta[r] + (bias ? bias[d] : 0.0));
@@ -182,13 +180,10 @@ int oracle_conv1d_f64(int64_t Bsz, int64_t Dm, int64_t L, int64_t K,
                       int nthreads) {
   if (Bsz < 0 || Dm < 0 || L < 0 || K < 1 || !x || !w || !u) return -1;
   const int64_t rows = Bsz * Dm, H = K - 1;
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-  (void)nthreads;
-#endif
+  const int nt = team_size(nthreads);
+  (void)nt;  /* unused without OpenMP */
   int bad = 0;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(nt)
   for (int64_t r = 0; r < rows; ++r) {
     const int64_t d = r % Dm;
     double* xe = (double*)malloc((size_t)(H + L + 1) * sizeof(double));
@@ -238,11 +233,8 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
   if (z && !dz) return -1;
   if (flags & ORACLE_ZOH) return -1;
   const int64_t rows = Bsz * Dm;
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#else
-  (void)nthreads;
-#endif
+  const int nt = team_size(nthreads);
+  (void)nt;  /* unused without OpenMP */
   /* per-row contributions to the channel and batch sums, reduced afterwards in row order */
   double* rA = (double*)calloc((size_t)(rows * N), sizeof(double));
   double* rD = (double*)calloc((size_t)rows, sizeof(double));
@@ -258,7 +250,7 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
   double* slab = (double*)malloc((size_t)(nch > 0 ? nch : 1) * (size_t)(2 * N * (L > 0 ? L : 1)) * sizeof(double));
   if (!slab) { free(rA); free(rD); free(rb); return -1; }
   for (int64_t b = 0; b < Bsz && !bad; ++b) {
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (int64_t c = 0; c < nch; ++c) {
       double* sB = slab + c * 2 * N * L;
       double* sC = sB + N * L;
