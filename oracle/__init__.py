@@ -109,7 +109,7 @@ class Oracle:
         return out, st
 
     def scan_bwd(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *, dout,
-                 dfinal=None, reverse=False, threads=0):
+                 dfinal=None, zoh=False, reverse=False, threads=0):
         """Gradients of the scan for output gradient dout [Bsz,Dm,L] (and final-state gradient
         dfinal [Bsz,Dm,N] or None).  Returns a dict with du, ddelta, dA, dB, dC and, when the
         matching input is given, dD, dz, ddelta_bias, dh0 (dh0 always: the gradient of the
@@ -129,7 +129,8 @@ class Oracle:
             Bsz, Dm, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(h0), _ptr(dout), _ptr(dfinal), _ptr(g["du"]), _ptr(g["ddelta"]),
             _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-            _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), REVERSE if reverse else 0, int(threads))
+            _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), (ZOH if zoh else 0) | (REVERSE if reverse else 0),
+            int(threads))
         if rc != 0:
             raise RuntimeError("oracle_scan_bwd_f64 failed (%d)" % rc)
         if D is None:

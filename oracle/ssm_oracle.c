@@ -64,7 +64,7 @@ static double softplus_f64(double x) {
 
 static double silu_f64(double z) { return z / (1.0 + exp(-z)); }
 
-int oracle_abi_version(void) { return 4; }
+int oracle_abi_version(void) { return 5; }
 
 /* Threads an OpenMP region of the oracle uses by default (1 without OpenMP). */
 int oracle_max_threads(void) {
@@ -202,18 +202,21 @@ int oracle_conv1d_f64(int64_t Bsz, int64_t Dm, int64_t L, int64_t K,
   return bad ? -1 : 0;
 }
 
-/* Gradients of the scan (default discretisation B_bar = dt*B; REVERSE allowed) for a
- * given output gradient dout [Bsz,Dm,L] and optional final-state gradient dfs
- * [Bsz,Dm,N].  Derived with the chain rule from the forward definition; with
- * G_n the gradient reaching h_n after step t (time order of the scan):
+/* Gradients of the scan (either discretisation, either direction) for a given output
+ * gradient dout [Bsz,Dm,L] and optional final-state gradient dfs [Bsz,Dm,N].  Derived
+ * with the chain rule from the forward definition.  Write B_bar = e * B, so e = dt by
+ * default and e = (Abar - 1) / A under ZOH (dt when A == 0); then de/ddt = 1 by default
+ * and Abar under ZOH, de/dA = 0 by default and (dt Abar - e) / A under ZOH (dt^2 / 2 at
+ * A == 0, the limit).  With G_n the gradient reaching h_n after step t (time order of the
+ * scan):
  *   dy_t   = dout_t * silu(z_t)                     (dout_t without z)
  *   dz_t   = dout_t * y_t * s(z_t) * (1 + z_t (1 - s(z_t))),  s = logistic
  *   G_n   += dy_t * C[n,t];   dC[b,n,t] += dy_t * h_t[n]
- *   du_t   = dy_t * D + sum_n G_n * dt_t * B[n,t]
+ *   du_t   = dy_t * D + sum_n G_n * e * B[n,t]
  *   dD    += dy_t * u_t
- *   ddt_t  = sum_n G_n * (h_{t-1}[n] * Abar * A[n] + u_t * B[n,t])
- *   dA[n] += G_n * h_{t-1}[n] * Abar * dt_t
- *   dB[b,n,t] += G_n * dt_t * u_t
+ *   ddt_t  = sum_n G_n * (h_{t-1}[n] * Abar * A[n] + de/ddt * u_t * B[n,t])
+ *   dA[n] += G_n * (h_{t-1}[n] * Abar * dt_t + de/dA * u_t * B[n,t])
+ *   dB[b,n,t] += G_n * e * u_t
  *   G_n    = G_n * Abar                             (on to h_{t-1})
  *   ddelta_t = ddt_t * s(x_t)   (softplus' = logistic);  dbias += ddelta_t
  *   dh0 = G after step 0 of the scan order.
@@ -231,7 +234,7 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
   if (Bsz < 0 || Dm < 0 || N <= 0 || L < 0) return -1;
   if (!u || !delta || !A || !Bm || !Cm || !dout || !du || !ddelta || !dA || !dB || !dC) return -1;
   if (z && !dz) return -1;
-  if (flags & ORACLE_ZOH) return -1;
+  const int zoh = (flags & ORACLE_ZOH) != 0;
   const int64_t rows = Bsz * Dm;
   const int nt = team_size(nthreads);
   (void)nt;  /* unused without OpenMP */
@@ -275,8 +278,10 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
           const double dt = softplus_f64(dr[t] + bd);
           double acc = 0.0;
           for (int64_t n = 0; n < N; ++n) {
-            const double a = exp(dt * A[d * N + n]);
-            const double h = a * hs[s * N + n] + dt * Ab[n * L + t] * ur[t];
+            const double an = A[d * N + n];
+            const double a = exp(dt * an);
+            const double e = (zoh && an != 0.0) ? (a - 1.0) / an : dt;
+            const double h = a * hs[s * N + n] + e * Ab[n * L + t] * ur[t];
             hs[(s + 1) * N + n] = h;
             acc += Cb[n * L + t] * h;
           }
@@ -302,12 +307,15 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
             const double an = A[d * N + n];
             const double a = exp(dt * an);
             const double hp = hs[s * N + n];
+            const double e = (zoh && an != 0.0) ? (a - 1.0) / an : dt;  /* B_bar / B */
+            const double e_dt = zoh ? a : 1.0;                             /* de/ddt */
+            const double e_dA = !zoh ? 0.0 : (an != 0.0 ? (dt * a - e) / an : 0.5 * dt * dt);
             G[n] += dy * Cb[n * L + t];
             sC[n * L + t] += dy * hs[(s + 1) * N + n];
-            dut += G[n] * dt * Ab[n * L + t];
-            ddt += G[n] * (hp * a * an + ur[t] * Ab[n * L + t]);
-            rA[r * N + n] += G[n] * hp * a * dt;
-            sB[n * L + t] += G[n] * dt * ur[t];
+            dut += G[n] * e * Ab[n * L + t];
+            ddt += G[n] * (hp * a * an + e_dt * ur[t] * Ab[n * L + t]);
+            rA[r * N + n] += G[n] * (hp * a * dt + e_dA * ur[t] * Ab[n * L + t]);
+            sB[n * L + t] += G[n] * e * ur[t];
             G[n] *= a;
           }
           du[r * L + t] = dut;

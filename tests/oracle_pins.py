@@ -403,7 +403,7 @@ def check_conv_causality(orc):
 
 # ---- gradients of the scan (chain rule on the forward definition; not on the pages) ----
 
-def _torch_forward(u, delta, A, B, C, D, z, delta_bias, h0, reverse=False):
+def _torch_forward(u, delta, A, B, C, D, z, delta_bias, h0, reverse=False, zoh=False):
     """A plain fp64 torch forward, written step by step over time with tensor ops over
     (batch, channel, state); its autograd gives gradients by a route independent of the
     oracle's hand-derived adjoint."""
@@ -416,7 +416,9 @@ def _torch_forward(u, delta, A, B, C, D, z, delta_bias, h0, reverse=False):
     outs = [None] * L
     for t in (range(L - 1, -1, -1) if reverse else range(L)):
         a = torch.exp(dt[:, :, t, None] * A[None])
-        h = a * h + dt[:, :, t, None] * B[:, None, :, t] * u[:, :, t, None]
+        # zero-order hold: B_bar = (exp(dt A) - 1) / A * B  (A is nonzero in these inputs)
+        e = torch.expm1(dt[:, :, t, None] * A[None]) / A[None] if zoh else dt[:, :, t, None]
+        h = a * h + e * B[:, None, :, t] * u[:, :, t, None]
         y = (h * C[:, None, :, t]).sum(-1)
         if D is not None:
             y = y + D[None, :] * u[:, :, t]
@@ -432,42 +434,44 @@ _GRAD_NAMES = [("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C",
 
 def check_bwd_autograd(orc):
     import torch
-    for reverse in (False, True):
-        inp = tiny_inputs(171 + reverse, L=25, h0=True)
+    for reverse, zoh in ((False, False), (True, False), (False, True), (True, True)):
+        inp = tiny_inputs(171 + reverse + 2 * zoh, L=25, h0=True)
         rng = np.random.default_rng(173)
         dout = rng.standard_normal(inp["u"].shape)
         dfin = rng.standard_normal(inp["h0"].shape)
         tin = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in inp.items()}
-        out, hL = _torch_forward(**tin, reverse=reverse)
-        y, h = orc.scan(**inp, reverse=reverse)
+        out, hL = _torch_forward(**tin, reverse=reverse, zoh=zoh)
+        y, h = orc.scan(**inp, reverse=reverse, zoh=zoh)
         assert rel(out.detach().numpy(), y) < 1e-13 and rel(hL.detach().numpy(), h) < 1e-13
         ((out * torch.from_numpy(dout)).sum() + (hL * torch.from_numpy(dfin)).sum()).backward()
-        g = orc.scan_bwd(**inp, dout=dout, dfinal=dfin, reverse=reverse)
+        g = orc.scan_bwd(**inp, dout=dout, dfinal=dfin, reverse=reverse, zoh=zoh)
         for k, gk in _GRAD_NAMES:
-            assert rel(g[gk], tin[k].grad.numpy()) < 1e-11, (reverse, gk, rel(g[gk], tin[k].grad.numpy()))
+            e = rel(g[gk], tin[k].grad.numpy())
+            assert e < 1e-11, (reverse, zoh, gk, e)
 
 
 def check_bwd_finite_difference(orc):
     """Directional derivatives of L = <dout, out> + <dfinal, h_L> from central differences of the
     forward oracle, one input at a time, against <gradient, direction>."""
-    inp = tiny_inputs(181, L=20, h0=True)
-    rng = np.random.default_rng(183)
-    dout = rng.standard_normal(inp["u"].shape)
-    dfin = rng.standard_normal(inp["h0"].shape)
-    g = orc.scan_bwd(**inp, dout=dout, dfinal=dfin)
+    for zoh in (False, True):
+        inp = tiny_inputs(181, L=20, h0=True)
+        rng = np.random.default_rng(183)
+        dout = rng.standard_normal(inp["u"].shape)
+        dfin = rng.standard_normal(inp["h0"].shape)
+        g = orc.scan_bwd(**inp, dout=dout, dfinal=dfin, zoh=zoh)
 
-    def loss(p):
-        y, h = orc.scan(**p)
-        return float(np.sum(y * dout) + np.sum(h * dfin))
+        def loss(p):
+            y, h = orc.scan(**p, zoh=zoh)
+            return float(np.sum(y * dout) + np.sum(h * dfin))
 
-    eps = 1e-5
-    for k, gk in _GRAD_NAMES:
-        v = rng.standard_normal(inp[k].shape)
-        lp = loss({**inp, k: inp[k] + eps * v})
-        lm = loss({**inp, k: inp[k] - eps * v})
-        fd = (lp - lm) / (2 * eps)
-        an = float(np.sum(g[gk] * v))
-        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gk, fd, an)
+        eps = 1e-5
+        for k, gk in _GRAD_NAMES:
+            v = rng.standard_normal(inp[k].shape)
+            lp = loss({**inp, k: inp[k] + eps * v})
+            lm = loss({**inp, k: inp[k] - eps * v})
+            fd = (lp - lm) / (2 * eps)
+            an = float(np.sum(g[gk] * v))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (zoh, gk, fd, an)
 
 
 def check_bwd_scalar_closed_form(orc):
@@ -488,10 +492,32 @@ def check_bwd_scalar_closed_form(orc):
     assert g["dC"][0, 0, 0] == 0.0
 
 
+def check_bwd_zoh_at_zero_decay(orc):
+    """ZOH with A = 0: B_bar = dt B and d(B_bar)/dA = dt^2 B / 2 (the series of (e^(dt A) - 1) / A).
+    One step from a zero state, L = out_0 = C h_1 = C dt B u:  dL/dA = C B u dt^2 / 2 and
+    dL/d(delta) = C B u * logistic(delta); a central difference over A = +-eps agrees."""
+    x = np.array([[[0.4]]])
+    u = np.array([[[1.3]]])
+    Bm = np.array([[[0.6]]])
+    Cm = np.array([[[-1.7]]])
+    A0 = np.array([[0.0]])
+    dt = np.logaddexp(0.0, 0.4)
+    g = orc.scan_bwd(u, x, A0, Bm, Cm, dout=np.array([[[1.0]]]), zoh=True)
+    want = Cm[0, 0, 0] * Bm[0, 0, 0] * u[0, 0, 0] * dt * dt / 2
+    assert abs(g["dA"][0, 0] - want) < 1e-15, (g["dA"], want)
+    sg = 1.0 / (1.0 + np.exp(-0.4))
+    assert abs(g["ddelta"][0, 0, 0] - Cm[0, 0, 0] * Bm[0, 0, 0] * u[0, 0, 0] * sg) < 1e-15
+    eps = 1e-4  # (e^(dt A) - 1) / A cancels near 0: rounding error ~1e-16 / eps, truncation ~eps^2
+    yp, _ = orc.scan(u, x, A0 + eps, Bm, Cm, zoh=True)
+    ym, _ = orc.scan(u, x, A0 - eps, Bm, Cm, zoh=True)
+    assert abs((yp - ym)[0, 0, 0] / (2 * eps) - want) < 1e-7
+
+
 ALL_CHECKS = [check_brute_force, check_initial_state, check_lti_closed_form, check_zoh_library,
               check_a_zero_cumsum, check_small_step_skip, check_single_step_closed_form,
               check_step_matches_scan, check_softplus_silu, check_linearity_in_u, check_causality,
               check_reverse, check_permutation_equivariance,
               check_conv_library, check_conv_impulse, check_conv_k1, check_conv_state_out,
               check_conv_chunking, check_conv_causality,
-              check_bwd_autograd, check_bwd_finite_difference, check_bwd_scalar_closed_form]
+              check_bwd_autograd, check_bwd_finite_difference, check_bwd_scalar_closed_form,
+              check_bwd_zoh_at_zero_decay]

@@ -51,11 +51,17 @@ MUTANTS = [
     ("conv_weight_row_stride", "v += w[d * K + k] * xe[t + k];", "v += w[k * Dm + d] * xe[t + k];"),
     ("bwd_adjoint_not_decayed", "          G[n] *= a;\n", "\n"),
     ("bwd_dC_uses_old_state", "sC[n * L + t] += dy * hs[(s + 1) * N + n];", "sC[n * L + t] += dy * hs[s * N + n];"),
-    ("bwd_dB_drops_u", "sB[n * L + t] += G[n] * dt * ur[t];", "sB[n * L + t] += G[n] * dt;"),
-    ("bwd_dA_drops_dt", "rA[r * N + n] += G[n] * hp * a * dt;", "rA[r * N + n] += G[n] * hp * a;"),
+    ("bwd_dB_drops_u", "sB[n * L + t] += G[n] * e * ur[t];", "sB[n * L + t] += G[n] * e;"),
+    ("bwd_dA_drops_dt", "rA[r * N + n] += G[n] * (hp * a * dt +", "rA[r * N + n] += G[n] * (hp * a +"),
     ("bwd_softplus_derivative", "const double dx = ddt / (1.0 + exp(-x));", "const double dx = ddt;"),
-    ("bwd_ddt_drops_decay_term", "ddt += G[n] * (hp * a * an + ur[t] * Ab[n * L + t]);",
-     "ddt += G[n] * (ur[t] * Ab[n * L + t]);"),
+    ("bwd_ddt_drops_decay_term", "ddt += G[n] * (hp * a * an + e_dt * ur[t] * Ab[n * L + t]);",
+     "ddt += G[n] * (e_dt * ur[t] * Ab[n * L + t]);"),
+    ("bwd_zoh_e_dt_is_one", "const double e_dt = zoh ? a : 1.0;", "const double e_dt = 1.0;"),
+    ("bwd_zoh_dA_term_dropped", "const double e_dA = !zoh ? 0.0 :", "const double e_dA = 1 ? 0.0 :"),
+    ("bwd_zoh_dA_sign", "(dt * a - e) / an", "(e - dt * a) / an"),
+    ("bwd_zoh_dA_limit", "0.5 * dt * dt);", "dt * dt);"),
+    ("bwd_zoh_forward_euler", "const double h = a * hs[s * N + n] + e * Ab[n * L + t] * ur[t];",
+     "const double h = a * hs[s * N + n] + dt * Ab[n * L + t] * ur[t];"),
     ("bwd_dz_silu_derivative", "sg * (1.0 + zr[t] * (1.0 - sg));", "sg;"),
     ("bwd_du_drops_skip", "double dut = dy * Dd;", "double dut = 0.0;"),
     ("bwd_adjoint_seed_ignored", "G[n] = dfs ? dfs[r * N + n] : 0.0;", "G[n] = 0.0;"),
