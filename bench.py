@@ -232,28 +232,32 @@ def bench_bwd(args, torch, ssm, W):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     grads = None
 
-    def call(x):
+    def call(x, zoh=False):
         nonlocal grads
         grads = ssm.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                             dout=x["dout"], grads=grads, workspace=ws)
+                             dout=x["dout"], grads=grads, workspace=ws, zoh=zoh)
 
-    for k in range(max(2, args.warmup)):
-        call(sets[k % R])
+    def timed(n, zoh):
+        for k in range(max(2, args.warmup)):
+            call(sets[k % R], zoh)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        torch.cuda.synchronize()
+        for k in range(n):
+            ev[2 * k].record()
+            call(sets[k % R], zoh)
+            ev[2 * k + 1].record()
+        torch.cuda.synchronize()
+        return sorted(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n))
+
     n = max(5, args.steps // 2)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
-    torch.cuda.synchronize()
-    for k in range(n):
-        ev[2 * k].record()
-        call(sets[k % R])
-        ev[2 * k + 1].record()
-    torch.cuda.synchronize()
-    ms = sorted(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n))
+    ms = timed(n, False)
     mean = sum(ms) / n
+    mz = timed(5, True)  # the zero-order-hold variant, same inputs (context, not the bench value)
     b = bwd_bytes(w)
     return {"workload": w.name, "rotated_input_sets": R, "call_ms": mean, "call_ms_median": ms[n // 2],
             "value": w.updates / (mean * 1e-3), "unit": "state-updates/s",
             "workspace_bytes": need, "algorithmic_bytes_per_call": b,
-            "hbm_GBs": b / (mean * 1e-3) / 1e9}
+            "hbm_GBs": b / (mean * 1e-3) / 1e9, "zoh_call_ms": sum(mz) / len(mz)}
 
 
 def conv_bytes(w, K) -> int:

@@ -156,8 +156,9 @@ size_t ssm_scan_bwd_workspace_size(const ssm_shape* shape);
  *   dz               : [B, D, L] io_dtype, required when z is given, else ignored
  *   dinitial_state   : [B, D, N] fp32 gradient of initial_state, NULL means not written
  *   workspace        : required, at least ssm_scan_bwd_workspace_size() bytes
- * shape->flags may hold SSM_FLAG_REVERSE; SSM_FLAG_ZOH is SSM_ERR_UNSUPPORTED.
- * No output may overlap an input, another output or the workspace.  Every sum is
+ * shape->flags may hold SSM_FLAG_REVERSE and SSM_FLAG_ZOH, as in the forward call
+ * (under ZOH the derivatives of B_bar = (exp(dt A) - 1) / A * B with respect to dt, A,
+ * B and u are taken, with the A -> 0 limit where A is zero).  No output may overlap an input, another output or the workspace.  Every sum is
  * taken in a fixed order, so results are bitwise reproducible. */
 ssm_status ssm_scan_bwd(const ssm_shape* shape,
                         const void* u, const void* delta, const float* A,

@@ -204,7 +204,7 @@ def bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SSM_BF16, reverse=Fa
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *, dout,
-             dfinal_state=None, reverse=False, grads=None, workspace=None, stream=None):
+             dfinal_state=None, zoh=False, reverse=False, grads=None, workspace=None, stream=None):
     """Gradients of scan_fwd for output gradient dout [B,D,L] (u's dtype) and optional
     final-state gradient [B,D,N] fp32.  Returns a dict: du, ddelta (u's dtype), dA [D,N], dB, dC
     [B,N,L], dD, ddelta_bias [D] (fp32), dz (u's dtype, None without z) and dinitial_state
@@ -214,7 +214,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     N = A.shape[1]
     io = _io_dtype(u)
     device = u.device
-    sh = make_shape(Bsz, Dm, N, L, io, False, reverse)
+    sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
     f32, dev = torch.float32, u.device
     for t, shp, dt, name in ((delta, (Bsz, Dm, L), u.dtype, "delta"), (A, (Dm, N), f32, "A"),
                              (B, (Bsz, N, L), u.dtype, "B"), (C, (Bsz, N, L), u.dtype, "C"),

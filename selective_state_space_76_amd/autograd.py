@@ -7,8 +7,8 @@
 Bookkeeping only: the forward and backward arithmetic both run in the library's HIP kernels (the
 gradients are the chain rule applied to the pages' forward recurrence, see include/ssm_scan.h).
 Gradients are returned in each input's dtype; the library computes dA, dB, dC, dD and d(delta_bias)
-in fp32 and they are cast to bf16 when those inputs are bf16.  The zero-order-hold discretisation
-has no backward in the library, so requesting gradients through it raises.
+in fp32 and they are cast to bf16 when those inputs are bf16.  Both discretisations (the default
+dt*B and zero-order hold) and both scan directions have gradients.
 """
 from __future__ import annotations
 
@@ -27,13 +27,11 @@ class SelectiveScanFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dout, dfinal):
-        if ctx.zoh:
-            raise NotImplementedError("gradients of the zero-order-hold variant are not provided")
         u, delta, A, B, C, D, z, delta_bias, initial_state = ctx.saved_tensors
         dout = torch.zeros_like(u) if dout is None else dout.to(u.dtype).contiguous()
         dfinal = None if dfinal is None else dfinal.float().contiguous()
         g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, initial_state, dout=dout, dfinal_state=dfinal,
-                     reverse=ctx.reverse)
+                     zoh=ctx.zoh, reverse=ctx.reverse)
         need = ctx.needs_input_grad
 
         def cast(grad, like, i):

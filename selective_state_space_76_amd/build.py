@@ -14,8 +14,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssmscan.so")
 SOURCES = [os.path.join(CSRC, f) for f in (
     "scan_bf16_out.hip", "scan_bf16_sum.hip", "scan_f32_out.hip", "scan_f32_sum.hip",
-    "ssm_kernels.hip", "conv_kernels.hip", "scan_bwd.hip", "ssm_abi.cpp")]
+    "ssm_kernels.hip", "conv_kernels.hip", "scan_bwd.hip", "scan_bwd_zoh.hip", "ssm_abi.cpp")]
 HEADERS = [os.path.join(CSRC, "ssm_launch.h"), os.path.join(CSRC, "ssm_device.h"),
+           os.path.join(CSRC, "scan_bwd_kernel.h"),
            os.path.join(ROOT, "include", "ssm_scan.h")]
 ARCH = "gfx950"
 

@@ -253,7 +253,6 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   if (!shape) return SSM_ERR_NULL;
   if (shape->io_dtype != SSM_F32 && shape->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (shape->flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE)) return SSM_ERR_UNSUPPORTED;
-  if (shape->flags & SSM_FLAG_ZOH) return SSM_ERR_UNSUPPORTED;
   BwdPlan pl;
   if (!make_bwd_plan(shape, &pl)) return SSM_ERR_SHAPE;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC || !workspace)
@@ -296,6 +295,7 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   float* part_d = reinterpret_cast<float*>(ws + pl.ckpt + pl.bc + pl.a);
   const int vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;
   const int rev = (shape->flags & SSM_FLAG_REVERSE) ? 1 : 0;
+  const int zoh = (shape->flags & SSM_FLAG_ZOH) ? 1 : 0;
 
   ssm::ScanParams fp;
   memset(&fp, 0, sizeof(fp));
@@ -307,6 +307,7 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   fp.nblk = (int)pl.nblk;
   fp.vec = vec;
   fp.reverse = rev;
+  fp.zoh = zoh;
   ssm_status rc = launch_status(ssm::launch_ckpt(fp, bf16, st));
   if (rc != SSM_OK) return rc;
 
@@ -320,6 +321,7 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   bp.nblk = (int)pl.nblk;
   bp.vec = vec;
   bp.reverse = rev;
+  bp.zoh = zoh;
   rc = launch_status(ssm::launch_bwd(bp, bf16, st));
   if (rc != SSM_OK) return rc;
 

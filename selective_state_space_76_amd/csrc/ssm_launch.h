@@ -70,6 +70,7 @@ struct BwdParams {
   int nblk;               // channel blocks of 16
   int vec;                // rows allow 16-byte vector loads
   int reverse;
+  int zoh;                // zero-order-hold B_bar
 };
 
 struct ConvParams {
@@ -90,6 +91,9 @@ hipError_t launch_carry(const ScanParams& p, hipStream_t s);
 // checkpoint pass (the scan kernel's mode 2), backward pass, and the fixed-order partial sums
 hipError_t launch_ckpt(const ScanParams& p, bool bf16, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
+// the zero-order-hold variants of the two (p.zoh set), compiled separately
+hipError_t launch_ckpt_zoh(const ScanParams& p, bool bf16, hipStream_t s);
+hipError_t launch_bwd_zoh(const BwdParams& p, bool bf16, hipStream_t s);
 // out[i] = sum_k part[k * stride + i] for i < n, k < count (k ascending)
 hipError_t launch_reduce(float* out, const float* part, int64_t count, int64_t stride, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);

@@ -201,7 +201,8 @@ def test_bwd_errors():
     for name in ("u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA", "dB", "dC", "ws"):
         assert bwd(shp(), **{name: None}) == 1, name
     assert bwd(shp(), z=fake(13)) == 1                      # z given without dz
-    assert bwd(shp(flags=L.SSM_FLAG_ZOH)) == 5              # ZOH gradients are not provided
+    assert bwd(shp(flags=L.SSM_FLAG_ZOH), du=fake(1, off=64)) == 8   # ZOH accepted, checks still run
+    assert bwd(shp(flags=L.SSM_FLAG_ZOH | 8)) == 5
     assert bwd(shp(flags=8)) == 5
     assert bwd(shp(io_dtype=3)) == 3
     assert bwd(shp(dstate=65)) == 2

@@ -16,9 +16,10 @@ DEV = "cuda"
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
-def test_autograd_matches_oracle(dtype, reverse):
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+def test_autograd_matches_oracle(dtype, reverse, zoh):
     name = "tiny" if dtype == torch.float32 else "mamba130m"
-    w = W.WORKLOADS[name].with_shape(batch=2, dim=40, dstate=16, seqlen=300, seed=8000 + reverse)
+    w = W.WORKLOADS[name].with_shape(batch=2, dim=40, dstate=16, seqlen=300, seed=8000 + reverse + 2 * zoh)
     x = W.scan_inputs(w)
     gen = torch.Generator().manual_seed(8100)
     h0 = torch.randn(w.batch, w.dim, w.dstate, generator=gen)
@@ -27,12 +28,12 @@ def test_autograd_matches_oracle(dtype, reverse):
     leaves = {k: v.to(DEV).requires_grad_(True) for k, v in x.items() if v is not None}
     h0g = h0.to(DEV).requires_grad_(True)
     out, fs = selective_scan(leaves["u"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"], leaves["D"],
-                             leaves["z"], leaves["delta_bias"], h0g, reverse=reverse)
+                             leaves["z"], leaves["delta_bias"], h0g, zoh=zoh, reverse=reverse)
     loss = (out.float() * wo.to(DEV).float()).sum() + (fs * wf.to(DEV)).sum()
     loss.backward()
     torch.cuda.synchronize()
     ref = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], h0,
-                          dout=wo, dfinal=wf, reverse=reverse)
+                          dout=wo, dfinal=wf, zoh=zoh, reverse=reverse)
     pairs = [("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"), ("z", "dz"),
              ("delta_bias", "ddelta_bias")]
     errs = {k: rel_err(leaves[k].grad, ref[gk]) for k, gk in pairs}
@@ -54,12 +55,3 @@ def test_autograd_only_final_state_used():
     ref = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                           dout=np.zeros(x["u"].shape), dfinal=np.ones((1, 16, 16)))
     assert rel_err(u.grad, ref["du"]) <= 1e-4
-
-
-def test_autograd_zoh_backward_refused():
-    w = W.WORKLOADS["tiny"].with_shape(batch=1, dim=16, seqlen=64, seed=8300)
-    x = W.scan_inputs(w)
-    u = x["u"].to(DEV).requires_grad_(True)
-    out, _ = selective_scan(u, x["delta"].to(DEV), x["A"].to(DEV), x["B"].to(DEV), x["C"].to(DEV), zoh=True)
-    with pytest.raises(NotImplementedError):
-        out.sum().backward()

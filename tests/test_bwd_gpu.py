@@ -39,18 +39,18 @@ def make(Bsz, Dm, N, L, dtype, seed, gate=True, skip=True, bias=True, h0=False, 
     return x
 
 
-def run(x, reverse=False):
+def run(x, reverse=False, zoh=False):
     d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
     g = scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], d["h0"],
-                 dout=d["dout"], dfinal_state=d["dfin"], reverse=reverse)
+                 dout=d["dout"], dfinal_state=d["dfin"], zoh=zoh, reverse=reverse)
     torch.cuda.synchronize()
     return g
 
 
-def check(x, reverse=False, tol=None):
-    g = run(x, reverse)
+def check(x, reverse=False, tol=None, zoh=False):
+    g = run(x, reverse, zoh)
     ref = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], x["h0"],
-                          dout=x["dout"], dfinal=x["dfin"], reverse=reverse)
+                          dout=x["dout"], dfinal=x["dfin"], zoh=zoh, reverse=reverse)
     tol = tol or tol_for(x["u"])
     errs = {}
     for k in NAMES:
@@ -89,6 +89,27 @@ def test_bwd_optional_operands_absent(dtype):
 def test_bwd_reverse(dtype, N):
     print("case: bwd reverse N=%d %s" % (N, dtype), flush=True)
     check(make(2, 17, N, 333, dtype, seed=40 + N, h0=True, dfin=True), reverse=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32, 64, 40])
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_bwd_zoh(dtype, N, reverse):
+    """Zero-order hold: B_bar = (exp(dt A) - 1) / A * B.  The inputs' dt A spans both sides of the
+    kernel's switch between the series and the closed form of (e^x - 1) / x and its derivative."""
+    print("case: bwd zoh N=%d %s reverse=%s 2x24x%dx201" % (N, dtype, reverse, N), flush=True)
+    check(make(2, 24, N, 201, dtype, seed=70 + N + reverse, h0=True, dfin=True), reverse=reverse, zoh=True)
+
+
+def test_bwd_zoh_zero_and_tiny_decay():
+    """ZOH with some A entries exactly 0 (B_bar = dt B, d B_bar / dA = dt^2 B / 2) and others tiny."""
+    x = make(2, 20, 16, 150, torch.float32, seed=77, h0=True, dfin=True)
+    A = x["A"].clone()
+    A[::3, ::2] = 0.0
+    A[1::3, 1::4] = -1e-4
+    x["A"] = A
+    print("case: bwd zoh with A = 0 and A = -1e-4 entries", flush=True)
+    check(x, zoh=True)
 
 
 def test_bwd_workload_mamba130m():
