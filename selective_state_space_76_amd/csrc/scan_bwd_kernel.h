@@ -50,15 +50,6 @@ __device__ __forceinline__ float rows4_sum2(float x, float y, float x2, float y2
 
 __device__ __forceinline__ float logistic_(float x) { return rcp_(1.0f + exp2_(-x * kLog2e)); }
 
-// Zero-order hold, with x = dt A, a = e^x and ia = 1 / A (per state, so no division per step):
-// zoh_e = B_bar / B = (e^x - 1) / A = dt phi(x), phi(x) = (e^x - 1) / x; below |x| = 0.03 from
-// phi's Taylor series to x^3 (the next term is under 1e-8 relative), above it (a - 1) / A,
-// where the rounding of a costs under 4e-6 relative.
-__device__ __forceinline__ float zoh_e(float dt, float x, float a, float ia) {
-  const float series = dt * (1.0f + x * (0.5f + x * (0.16666667f + x * 0.041666668f)));
-  return (fabsf(x) < 0.03f) ? series : (a - 1.0f) * ia;
-}
-
 // d(zoh_e)/dA = (dt a - zoh_e) / A = dt^2 phi'(x), phi'(x) = sum_k (k + 1) x^k / (k + 2)!.
 // Below |x| = 1/4 from the series to x^5 (the next term is under 1e-7 relative there); above
 // it the closed form, whose difference dt a - zoh_e ~ dt x / 2 is then large enough that

@@ -72,10 +72,14 @@ __device__ __forceinline__ float softplus_(float x) {
 
 __device__ __forceinline__ float silu_(float z) { return z * rcp_(1.0f + exp2_(-z * kLog2e)); }
 
-// (exp(x) - 1) / x, accurate near 0 (Taylor terms to x^3 when |x| < 0.03).
-__device__ __forceinline__ float expm1_over_x(float x, float ex) {
-  const float series = 1.0f + x * (0.5f + x * (0.16666667f + x * 0.041666668f));
-  return (fabsf(x) < 0.03f) ? series : (ex - 1.0f) * rcp_(x);
+// Zero-order hold: B_bar / B = (e^x - 1) / A = dt phi(x) with x = dt A, a = e^x and ia = 1 / A
+// (taken once per state where A is fixed, so no division per step), phi(x) = (e^x - 1) / x.
+// Below |x| = 0.03 from phi's Taylor series to x^3 (the next term is under 1e-8 relative);
+// above it (a - 1) / A, where the rounding of a costs under 4e-6 relative.  A = 0 takes the
+// series branch (ia is then infinite and its product discarded).
+__device__ __forceinline__ float zoh_e(float dt, float x, float a, float ia) {
+  const float series = dt * (1.0f + x * (0.5f + x * (0.16666667f + x * 0.041666668f)));
+  return (fabsf(x) < 0.03f) ? series : (a - 1.0f) * ia;
 }
 
 template <int V> struct IC { static constexpr int value = V; };
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
   const float biasd = p.bias ? p.bias[dd] : 0.0f;
   const float Dd = p.D ? p.D[dd] : 0.0f;
 
-  float Ap[NL], Aln[NL], h[NL];
+  float Ap[NL], Aln[NL], Ainv[NL], h[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int64_t n = g + 16 * i;
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
     const float a = p.A[dd * N + nn];
     Aln[i] = nv ? a : 0.0f;
     Ap[i] = Aln[i] * kLog2e;
+    Ainv[i] = ZOH ? 1.0f / Aln[i] : 0.0f;
     float h0 = 0.0f;
     if (MODE != 1) {
       if (MODE == 0 && p.carries) h0 = p.carries[(((int64_t)seg * p.Bsz + b) * Dm + dd) * N + nn];
@@ -402,6 +407,53 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
     if (PREF) read_bc(0, bcur, ccur);
 
     float ys[4];
+    if constexpr (ZOH) {
+      // The ZOH factor makes phase A larger; fully unrolled, the compiler hoists it across sub-blocks
+      // and slices and spills.  So the sub-blocks run in a rolled loop and each state slice fuses its
+      // factors with its chain, reading its B/C just before use.
+#pragma unroll 1
+      for (int s = 0; s < 4; ++s) {
+        const float dls = s == 0 ? dl[0] : (s == 1 ? dl[1] : (s == 2 ? dl[2] : dl[3]));
+        const float xus = s == 0 ? xu[0] : (s == 1 ? xu[1] : (s == 2 ? xu[2] : xu[3]));
+        float pj[16];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          // an empty asm that takes the previous slice's end state and hands on this slice's step
+          // values: the slices then run one after the other instead of being hoisted together
+          float dli = dls, xui = xus;
+          if (i > 0) asm volatile("" : "+v"(dli), "+v"(xui) : "v"(h[i > 0 ? i - 1 : 0]) : "memory");
+          float bb[16], cc[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 vb = *reinterpret_cast<const float4*>(Bt + (g + 16 * i) * TS + 16 * s + 4 * q);
+            bb[4 * q] = vb.x; bb[4 * q + 1] = vb.y; bb[4 * q + 2] = vb.z; bb[4 * q + 3] = vb.w;
+            if (MODE == 0) {
+              const float4 vc = *reinterpret_cast<const float4*>(Ct + (g + 16 * i) * TS + 16 * s + 4 * q);
+              cc[4 * q] = vc.x; cc[4 * q + 1] = vc.y; cc[4 * q + 2] = vc.z; cc[4 * q + 3] = vc.w;
+            }
+          }
+          float hi = h[i];
+          static_for<0, 16>([&](auto j_) {
+            constexpr int j = decltype(j_)::value;
+            const float dj = row_bcast<j>(dli);
+            const float a = exp2_(dj * Ap[i]);
+            const float x = zoh_e(dj, dj * Aln[i], a, Ainv[i]) * (row_bcast<j>(xui) * bb[j]);
+            hi = __builtin_fmaf(a, hi, x);
+            if (MODE == 0) pj[j] = (i == 0) ? cc[j] * hi : __builtin_fmaf(cc[j], hi, pj[j]);
+          });
+          h[i] = hi;
+        }
+        if (MODE == 0) {
+          const float uus = s == 0 ? uu[0] : (s == 1 ? uu[1] : (s == 2 ? uu[2] : uu[3]));
+          const float gzs = s == 0 ? gz[0] : (s == 1 ? gz[1] : (s == 2 ? gz[2] : gz[3]));
+          const float yv = (row_transpose_sum(pj) + Dd * uus) * gzs;
+          ys[0] = s == 0 ? yv : ys[0];
+          ys[1] = s == 1 ? yv : ys[1];
+          ys[2] = s == 2 ? yv : ys[2];
+          ys[3] = s == 3 ? yv : ys[3];
+        }
+      }
+    } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (PREF) {
@@ -420,7 +472,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
           const float bv = bcur[i][j];
           const float a = exp2_(dj * Ap[i]);
           av[j][i] = a;
-          if (ZOH) xv[j][i] = (dj * expm1_over_x(dj * Aln[i], a)) * (xj * bv);
+          if (ZOH) xv[j][i] = zoh_e(dj, dj * Aln[i], a, Ainv[i]) * (xj * bv);
           else xv[j][i] = xj * bv;
         }
       });
@@ -446,6 +498,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
 #pragma unroll
           for (int j = 0; j < 16; ++j) { bcur[i][j] = bnxt[i][j]; ccur[i][j] = cnxt[i][j]; }
       }
+    }
     }
     if (MODE == 0 && dval) {
 #pragma unroll
@@ -537,7 +590,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   for (int k = 0; k < 4; ++k) {
     const float a = exp2_(dt * Av[k] * kLog2e);
     float x;
-    if (ZOH) x = (dt * expm1_over_x(dt * Av[k], a)) * (xu * Bv[k]);
+    if (ZOH) x = zoh_e(dt, dt * Av[k], a, rcp_(Av[k])) * (xu * Bv[k]);
     else x = xu * Bv[k];
     hv[k] = __builtin_fmaf(a, hv[k], x);
     acc = __builtin_fmaf(Cv[k], hv[k], acc);
@@ -629,7 +682,7 @@ __global__ __launch_bounds__(256) void step4_kernel(StepParams p) {
     for (int e = 0; e < 4; ++e) {
       const float a = exp2_(dt * Av[e] * kLog2e);
       float x;
-      if (ZOH) x = (dt * expm1_over_x(dt * Av[e], a)) * (xu * Bv[k][e]);
+      if (ZOH) x = zoh_e(dt, dt * Av[e], a, rcp_(Av[e])) * (xu * Bv[k][e]);
       else x = xu * Bv[k][e];
       hn[e] = __builtin_fmaf(a, hv[e], x);
       acc = __builtin_fmaf(lv[k] ? Cv[k][e] : 0.0f, hn[e], acc);  // padding quads add nothing

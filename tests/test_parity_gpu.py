@@ -180,6 +180,22 @@ def test_reverse(dtype, L):
     full_check(x, h0=h0, reverse=True)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N", [32, 40, 64])
+def test_zoh_state_slices(dtype, N):
+    """ZOH with two and four state slices per lane, ragged length, with an initial state."""
+    print("case: zoh N=%d %s 2x24x%dx1001" % (N, dtype, N), flush=True)
+    x = make(2, 24, N, 1001, dtype=dtype, seed=300 + N)
+    h0 = torch.randn(2, 24, N, generator=torch.Generator().manual_seed(N))
+    full_check(x, h0=h0, zoh=True)
+
+
+def test_zoh_split_wide_state():
+    """ZOH through the sequence split (summary, carry and output passes) with 64 states."""
+    print("case: zoh split N=64 1x40x64x4500", flush=True)
+    full_check(make(1, 40, 64, 4500, seed=77), zoh=True)
+
+
 def test_reverse_zoh_wide_state():
     print("case: reverse+zoh N=64", flush=True)
     full_check(make(2, 20, 64, 700, dtype=torch.float32, seed=99), zoh=True, reverse=True)
