@@ -284,39 +284,48 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
     }
 
     float dug[4], ddg[4], dzg[4];
-#pragma unroll
+    // with several state slices the sub-blocks run in a rolled loop: unrolled, the compiler
+    // interleaves their independent work and runs out of registers
+    constexpr int SUNR = NL > 1 ? 1 : 4;
+#pragma unroll SUNR
     for (int s = 3; s >= 0; --s) {
-      // forward through the sub-block for y.  With one state slice (NL == 1) the states and
-      // decay factors are kept for the backward sweep; with more, each slice is recomputed
-      // right before its backward sweep so only one slice is ever held in registers.
+      auto pick = [&](const float (&v)[4]) { return s == 0 ? v[0] : (s == 1 ? v[1] : (s == 2 ? v[2] : v[3])); };
+      const float dt_s = pick(dt), xu_s = pick(xu), uu_s = pick(uu), go_s = pick(go), zz_s = pick(zz),
+                  xs_s = pick(xs);
+      float hs_s[NL];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) hs_s[i] = s == 0 ? hs[0][i] : (s == 1 ? hs[1][i] : (s == 2 ? hs[2][i] : hs[3][i]));
+      float dug_s, ddg_s, dzg_s;
+      // The states of the sub-block.  With one state slice (NL == 1) a forward pass keeps the
+      // states and decay factors for the sweep and gives y; with more, each slice is recomputed
+      // right before its own sweep (only one slice is ever held in registers) and adds its part
+      // of y there: the sweep needs dy = dout silu(z), not y, which only dz uses.
       float hv[16], av[16];
       float pj[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) pj[j] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        float h = hs[s][i];
-        const float* brow = Bt + (g + 16 * i) * TS + 16 * s;
-        const float* crow = Ct + (g + 16 * i) * TS + 16 * s;
+      if constexpr (KEEP_A) {
+        float h = hs_s[0];
+        const float* brow = Bt + g * TS + 16 * s;
+        const float* crow = Ct + g * TS + 16 * s;
         static_for<0, 16>([&](auto j_) {
           constexpr int j = decltype(j_)::value;
-          const float dj = row_bcast<j>(dt[s]);
-          const float a = exp2_(dj * Ap[i]);
-          h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xu[s]), brow[j], a, i));
-          if constexpr (KEEP_A) {
-            av[j] = a;
-            hv[j] = h;
-          }
+          const float dj = row_bcast<j>(dt_s);
+          const float a = exp2_(dj * Ap[0]);
+          h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xu_s), brow[j], a, 0));
+          av[j] = a;
+          hv[j] = h;
           pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
         });
       }
-      const float y = row_transpose_sum(pj) + Dd * uu[s];  // this lane's step, before the gate
-      float dy = go[s];
-      dzg[s] = 0.0f;
+      float ykeep = 0.0f;
+      if constexpr (KEEP_A) ykeep = row_transpose_sum(pj) + Dd * uu_s;  // y now: pj is not held through the sweep
+      float dy = go_s, sg = 0.0f;
+      dzg_s = 0.0f;
       if (has_z) {
-        const float sg = logistic_(zz[s]);
-        dy = go[s] * (zz[s] * sg);
-        dzg[s] = go[s] * y * (sg * __builtin_fmaf(zz[s], 1.0f - sg, 1.0f));
+        sg = logistic_(zz_s);
+        dy = go_s * (zz_s * sg);
+        if constexpr (KEEP_A) dzg_s = go_s * ykeep * (sg * __builtin_fmaf(zz_s, 1.0f - sg, 1.0f));
       }
 
       // backwards through the sub-block
@@ -329,14 +338,19 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
         const float* brow = Bt + (g + 16 * i) * TS + 16 * s;
         const float* crow = Ct + (g + 16 * i) * TS + 16 * s;
         if constexpr (!KEEP_A) {
-          float h = hs[s][i];
+          // recompute this slice's states (and its part of y); the empty asm orders the slices
+          // one after another so the compiler does not interleave them and run out of registers
+          float dts = dt_s, xus = xu_s;
+          asm volatile("" : "+v"(dts), "+v"(xus) : "v"(G[i > 0 ? i - 1 : 0]) : "memory");
+          float h = hs_s[i];
           static_for<0, 16>([&](auto j_) {
             constexpr int j = decltype(j_)::value;
-            const float dj = row_bcast<j>(dt[s]);
+            const float dj = row_bcast<j>(dts);
             const float a = exp2_(dj * Ap[i]);
-            h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xu[s]), brow[j], a, i));
+            h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xus), brow[j], a, i));
             av[j] = a;
             hv[j] = h;
+            pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
           });
         }
         float Gi = G[i], dAi = dAacc[i];
@@ -347,13 +361,13 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
           Gi = __builtin_fmaf(dyj, crow[j], Gi);
           const float yc = dyj * hv[j];
           const float a = av[j];
-          const float hp = j > 0 ? hv[j > 0 ? j - 1 : 0] : hs[s][i];
+          const float hp = j > 0 ? hv[j > 0 ? j - 1 : 0] : hs_s[i];
           const float tt = Gi * hp * a;
           float xb;  // dB contribution
           if constexpr (ZOH) {
             // s1: sum G e B (du);  s2: sum G Abar (h_{t-1} A + u B) (ddt)
-            const float dj = row_bcast<j>(dt[s]);
-            const float uj = row_bcast<j>(xu[s]);
+            const float dj = row_bcast<j>(dt_s);
+            const float uj = row_bcast<j>(xu_s);
             const float x = dj * Aln[i];
             const float e = zoh_e(dj, x, a, Ainv[i]);
             const float gb = Gi * brow[j];
@@ -366,8 +380,8 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
             // s1: sum G B;  s2: sum G Abar h_{t-1} A
             s1[j] = __builtin_fmaf(Gi, brow[j], s1[j]);
             s2[j] = __builtin_fmaf(tt, Aln[i], s2[j]);
-            dAi = __builtin_fmaf(tt, row_bcast<j>(dt[s]), dAi);
-            xb = Gi * row_bcast<j>(xu[s]);
+            dAi = __builtin_fmaf(tt, row_bcast<j>(dt_s), dAi);
+            xb = Gi * row_bcast<j>(xu_s);
           }
           Gi = Gi * a;
           if constexpr (j % 2 == 1) {
@@ -383,15 +397,19 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
         G[i] = Gi;
         dAacc[i] = dAi;
       }
+      if constexpr (!KEEP_A) {
+        const float y = row_transpose_sum(pj) + Dd * uu_s;  // this lane's step, before the gate
+        if (has_z) dzg_s = go_s * y * (sg * __builtin_fmaf(zz_s, 1.0f - sg, 1.0f));
+      }
       const float S1 = row_transpose_sum(s1);
       const float S2 = row_transpose_sum(s2);
       const int64_t t = t0 + 16 * s + g;
-      dug[s] = ZOH ? dy * Dd + S1 : dy * Dd + dt[s] * S1;
-      const float ddt = ZOH ? S2 : uu[s] * S1 + S2;
-      ddg[s] = ddt * logistic_(xs[s]);
+      dug_s = ZOH ? dy * Dd + S1 : dy * Dd + dt_s * S1;
+      const float ddt = ZOH ? S2 : uu_s * S1 + S2;
+      ddg_s = ddt * logistic_(xs_s);
       if (t < L) {
-        dbacc += ddg[s];
-        dDacc = __builtin_fmaf(dy, uu[s], dDacc);
+        dbacc += ddg_s;
+        dDacc = __builtin_fmaf(dy, uu_s, dDacc);
       }
 
       // the workgroup's dB/dC for these 16 steps: add the 4 waves' sums in order
@@ -407,6 +425,12 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
         }
       }
       sbp ^= 1;  // the next sub-block writes the other buffer; this one is free after the next barrier
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dug[k] = k == s ? dug_s : dug[k];
+        ddg[k] = k == s ? ddg_s : ddg[k];
+        dzg[k] = k == s ? dzg_s : dzg[k];
+      }
     }
     if (dval) {
 #pragma unroll
