@@ -301,6 +301,7 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
       // right before its own sweep (only one slice is ever held in registers) and adds its part
       // of y there: the sweep needs dy = dout silu(z), not y, which only dz uses.
       float hv[16], av[16];
+      float ev[ZOH ? 16 : 1], edv[ZOH ? 16 : 1];  // ZOH: B_bar / B and its A-derivative per step
       float pj[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) pj[j] = 0.0f;
@@ -312,7 +313,15 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
           constexpr int j = decltype(j_)::value;
           const float dj = row_bcast<j>(dt_s);
           const float a = exp2_(dj * Ap[0]);
-          h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xu_s), brow[j], a, 0));
+          if constexpr (ZOH) {
+            const float x = dj * Aln[0];
+            const float e = zoh_e(dj, x, a, Ainv[0]);
+            ev[j] = e;
+            edv[j] = zoh_e_dA(dj, x, a, e, Ainv[0]);
+            h = __builtin_fmaf(a, h, e * (row_bcast<j>(xu_s) * brow[j]));
+          } else {
+            h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xu_s), brow[j], a, 0));
+          }
           av[j] = a;
           hv[j] = h;
           pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
@@ -347,7 +356,15 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
             constexpr int j = decltype(j_)::value;
             const float dj = row_bcast<j>(dts);
             const float a = exp2_(dj * Ap[i]);
-            h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xus), brow[j], a, i));
+            if constexpr (ZOH) {
+              const float x = dj * Aln[i];
+              const float e = zoh_e(dj, x, a, Ainv[i]);
+              ev[j] = e;
+              edv[j] = zoh_e_dA(dj, x, a, e, Ainv[i]);
+              h = __builtin_fmaf(a, h, e * (row_bcast<j>(xus) * brow[j]));
+            } else {
+              h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xus), brow[j], a, i));
+            }
             av[j] = a;
             hv[j] = h;
             pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
@@ -368,13 +385,12 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
             // s1: sum G e B (du);  s2: sum G Abar (h_{t-1} A + u B) (ddt)
             const float dj = row_bcast<j>(dt_s);
             const float uj = row_bcast<j>(xu_s);
-            const float x = dj * Aln[i];
-            const float e = zoh_e(dj, x, a, Ainv[i]);
+            const float e = ev[j];
             const float gb = Gi * brow[j];
             const float gbu = gb * uj;
             s1[j] = __builtin_fmaf(gb, e, s1[j]);
             s2[j] = __builtin_fmaf(tt, Aln[i], __builtin_fmaf(gbu, a, s2[j]));
-            dAi = __builtin_fmaf(tt, dj, __builtin_fmaf(gbu, zoh_e_dA(dj, x, a, e, Ainv[i]), dAi));
+            dAi = __builtin_fmaf(tt, dj, __builtin_fmaf(gbu, edv[j], dAi));
             xb = Gi * (e * uj);
           } else {
             // s1: sum G B;  s2: sum G Abar h_{t-1} A
