@@ -615,10 +615,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
 }
 
 // Decode step when N is a multiple of 4: G lanes per channel (G >= N/4, a power of two) with 4
-// states each, and U channel slots per thread.  Every slot's loads (the state with a nontemporal
-// 16-byte access, A, B, C and the channel's delta/u/z) are issued before any arithmetic, so each lane
-// keeps U x 16 bytes of state in flight; slot k of a workgroup lies 256 lanes after slot k-1, so every
-// load instruction still covers contiguous memory.
+// states each, and U slots per lane: the same channel and state quad in U batch rows ceil(B/U)
+// apart, so the lane reads its A quad once for all of them.  Every slot's loads (the state with a
+// nontemporal 16-byte access, B, C and the channel's delta/u/z) are issued before any arithmetic,
+// so each lane keeps U x 16 bytes of state in flight; each load instruction of a wave still covers
+// contiguous memory (consecutive lanes, consecutive channels of one batch row).
 template <typename IO, int G, int U, bool ZOH>
 __global__ __launch_bounds__(256) void step4_kernel(StepParams p) {
   const int64_t BD = p.Bsz * p.Dm;
@@ -634,20 +635,28 @@ __global__ __launch_bounds__(256) void step4_kernel(StepParams p) {
   int qs[U];
   bool cvs[U], lv[U];
   const void* zsrc = p.z ? p.z : p.u;  // without a gate the loaded value is unused
+  // the U slots of a lane are the same channel d and state quad in U batch rows BU apart, so A is
+  // read once per lane
+  const int64_t BU = (p.Bsz + U - 1) / U;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t c0 = gid / G;
+  const int q0 = (int)(gid % G);
+  const bool c0v = c0 < BU * p.Dm;
+  const int64_t c0c = c0v ? c0 : 0;
+  const int64_t b0 = c0c / p.Dm, d0 = c0c - b0 * p.Dm;
+  const int64_t n00 = 4 * (int64_t)q0;
+  const int64_t nc0 = n00 < N ? n00 : 0;
+  const float4 aq0 = *reinterpret_cast<const float4*>(p.A + d0 * N + nc0);
 #pragma unroll
   for (int k = 0; k < U; ++k) {
-    const int64_t gid = ((int64_t)blockIdx.x * U + k) * 256 + threadIdx.x;
-    const int64_t c = gid / G;
-    const int q = (int)(gid % G);
-    const bool cval = c < BD;
-    const int64_t cc = cval ? c : BD - 1;
-    const int64_t b = cc / p.Dm, d = cc - b * p.Dm;
-    const int64_t n0 = 4 * (int64_t)q;
-    const bool live = cval && n0 < N;
-    const int64_t nc = n0 < N ? n0 : 0;
-    ccs[k] = cc; n0s[k] = nc; qs[k] = q; cvs[k] = cval; lv[k] = live;
+    const int64_t bk = b0 + k * BU;
+    const bool cval = c0v && bk < p.Bsz;
+    const int64_t cc = cval ? bk * p.Dm + d0 : BD - 1;
+    const int64_t b = cc / p.Dm;
+    const int64_t nc = nc0;
+    ccs[k] = cc; n0s[k] = nc; qs[k] = q0; cvs[k] = cval; lv[k] = cval && n00 < N;
     hq[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.state + cc * N + nc));
-    aq[k] = *reinterpret_cast<const float4*>(p.A + d * N + nc);
+    aq[k] = aq0;
     const IO* Bp = reinterpret_cast<const IO*>(p.B) + b * N + nc;
     const IO* Cp = reinterpret_cast<const IO*>(p.C) + b * N + nc;
     if constexpr (sizeof(IO) == 2) {  // 4 bf16 states = one 8-byte load each
@@ -666,8 +675,8 @@ __global__ __launch_bounds__(256) void step4_kernel(StepParams p) {
     dlv[k] = to_f32(reinterpret_cast<const IO*>(p.delta)[cc]);
     uvv[k] = to_f32(reinterpret_cast<const IO*>(p.u)[cc]);
     zvv[k] = to_f32(reinterpret_cast<const IO*>(zsrc)[cc]);
-    bsv[k] = p.bias ? p.bias[d] : 0.0f;
-    dsv[k] = p.D ? p.D[d] : 0.0f;
+    bsv[k] = p.bias ? p.bias[d0] : 0.0f;
+    dsv[k] = p.D ? p.D[d0] : 0.0f;
   }
 #pragma unroll
   for (int k = 0; k < U; ++k) {

@@ -49,9 +49,9 @@ static hipError_t launch_step_g(const StepParams& p, hipStream_t s) {
 
 template <typename IO, int G>
 static hipError_t launch_step4_g(const StepParams& p, hipStream_t s) {
-  constexpr int U = 2;  // channel slots per thread (measured best of 1, 2, 4 at 256 x 5120 x 16)
-  const int64_t lanes = p.Bsz * p.Dm * G;
-  const dim3 grid((unsigned)((lanes + 256 * U - 1) / (256 * U)));
+  constexpr int U = 2;  // batch rows per lane (measured best of 2, 4, 8 at 256 x 5120 x 16)
+  const int64_t lanes = (p.Bsz + U - 1) / U * p.Dm * G;  // each lane serves U batch rows of one channel
+  const dim3 grid((unsigned)((lanes + 255) / 256));
   if (p.zoh) hipLaunchKernelGGL((step4_kernel<IO, G, U, true>), grid, dim3(256), 0, s, p);
   else hipLaunchKernelGGL((step4_kernel<IO, G, U, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
