@@ -114,7 +114,20 @@ def bench_scan(args, torch, ssm, W):
     launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     ms_step = (t1 - t0) * 1e3 / args.steps
     mean_launch = sum(launch_ms) / len(launch_ms)
-    return w, R, ms_step, mean_launch, launch_ms, sets[0]
+    # the same launch with L2 and the Infinity Cache flushed before each rep (a 1 GiB fill outside
+    # the events), as a cross-check of the rotation above
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    nf = min(args.steps, 20)
+    fs_, fe_ = [torch.cuda.Event(enable_timing=True) for _ in range(nf)], [torch.cuda.Event(enable_timing=True) for _ in range(nf)]
+    for k in range(nf):
+        flush.zero_()
+        fs_[k].record()
+        call(sets[k % R])
+        fe_[k].record()
+    torch.cuda.synchronize()
+    flushed = sorted(s_.elapsed_time(e_) for s_, e_ in zip(fs_, fe_))
+    del flush
+    return w, R, ms_step, mean_launch, launch_ms, sets[0], flushed
 
 
 def bench_decode(args, torch, ssm, W):
@@ -456,7 +469,7 @@ def main():
     from selective_state_space_76_amd import workloads as W
     ssm.load()
 
-    w, R, ms_step, launch_ms, all_launch, x0 = bench_scan(args, torch, ssm, W)
+    w, R, ms_step, launch_ms, all_launch, x0, flushed = bench_scan(args, torch, ssm, W)
     upd = w.updates
     b = scan_bytes(w)
     value = upd / (ms_step * 1e-3)
@@ -475,7 +488,10 @@ def main():
                      "ops_per_update": OPS_PER_UPDATE, "launch_ms": launch_ms,
                      "launch_ms_median": all_launch[len(all_launch) // 2],
                      "launch_ms_p10": all_launch[len(all_launch) // 10],
-                     "launch_ms_p90": all_launch[(9 * len(all_launch)) // 10]},
+                     "launch_ms_p90": all_launch[(9 * len(all_launch)) // 10],
+                     "flushed_launch_ms_median": flushed[len(flushed) // 2],
+                     "flushed_launch_ms_p10": flushed[len(flushed) // 10],
+                     "flushed_launch_ms_p90": flushed[(9 * len(flushed)) // 10]},
         "hbm": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                 "algorithmic_bytes_per_launch": b},
         "kernel_source_hash": kernel_source_hash(),
