@@ -68,7 +68,7 @@ def step_bytes(w) -> int:
 
 
 def traffic_from_profile(workload: str, launches_per_call: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this build."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the built kernels."""
     path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
     if not os.path.exists(path):
         return None
@@ -448,7 +448,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan shards over (batch, channel) with no exchange, so "
-              "a multi-GPU figure is not produced by this build (run with --gpus 1)", file=sys.stderr)
+              "no multi-GPU figure is produced (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
