@@ -497,6 +497,9 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "input_fp64_sums": {k: float(v.double().sum()) for k, v in x0.items()
                             if v is not None and k not in ("out", "fs")},
+        "input_hash64": {k: hashlib.blake2b(v.contiguous().view(torch.uint8).cpu().numpy().tobytes(),
+                                            digest_size=8).hexdigest()
+                         for k, v in x0.items() if v is not None and k not in ("out", "fs")},
     }
     cp = copy_peak(torch)
     res["hbm"]["copy_peak_GBs"] = cp
