@@ -14,8 +14,9 @@
 //   ddelta_t = ddt_t * logistic(delta_t + bias);  dbias += ddelta_t;  dD += dy_t u_t
 //   dh0 = G after the first step.
 //
-// Work layout: the forward kernel's (a workgroup = 16 channels of one batch row, a
-// 16-lane row = one channel, lane g holds states g + 16 i).  A checkpoint pass
+// Work layout (up to 16 states; more states run in chunk_bwd_kernel, scan_bwd_chunk.h): the
+// forward kernel's (a workgroup = 16 channels of one batch row, a 16-lane row = one
+// channel, lane g holds state g).  A checkpoint pass
 // (the scan kernel's mode 2) stores the state entering every 64-step block.  This
 // kernel walks the blocks from last to first: it restores the block's states from
 // the checkpoint by recomputing the forward recurrence in 16-step sub-blocks, then
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
   constexpr int CPT = (NCH + 255) / 256;
   constexpr int TILE = NT * NP * TS + NS * 16 * TS;
   constexpr int RED = 4 * 2 * 16 * NP;         // per-wave dB/dC sums of one sub-block
-  constexpr bool KEEP_A = NL == 1;             // keep a sub-block's states and decay factors from the y pass
+  static_assert(NL == 1, "more than 16 states run in chunk_bwd_kernel");
   __shared__ __attribute__((aligned(16))) float tiles[TILE];
   __shared__ float red[2 * RED];               // double-buffered by sub-block parity
 
@@ -284,10 +285,7 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
     }
 
     float dug[4], ddg[4], dzg[4];
-    // with several state slices the sub-blocks run in a rolled loop: unrolled, the compiler
-    // interleaves their independent work and runs out of registers
-    constexpr int SUNR = NL > 1 ? 1 : 4;
-#pragma unroll SUNR
+#pragma unroll
     for (int s = 3; s >= 0; --s) {
       auto pick = [&](const float (&v)[4]) { return s == 0 ? v[0] : (s == 1 ? v[1] : (s == 2 ? v[2] : v[3])); };
       const float dt_s = pick(dt), xu_s = pick(xu), uu_s = pick(uu), go_s = pick(go), zz_s = pick(zz),
@@ -296,16 +294,14 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
 #pragma unroll
       for (int i = 0; i < NL; ++i) hs_s[i] = s == 0 ? hs[0][i] : (s == 1 ? hs[1][i] : (s == 2 ? hs[2][i] : hs[3][i]));
       float dug_s, ddg_s, dzg_s;
-      // The states of the sub-block.  With one state slice (NL == 1) a forward pass keeps the
-      // states and decay factors for the sweep and gives y; with more, each slice is recomputed
-      // right before its own sweep (only one slice is ever held in registers) and adds its part
-      // of y there: the sweep needs dy = dout silu(z), not y, which only dz uses.
+      // The states of the sub-block: a forward pass keeps the states and decay factors for the
+      // sweep and gives y (which only dz needs; the sweep needs dy = dout silu(z)).
       float hv[16], av[16];
       float ev[ZOH ? 16 : 1], edv[ZOH ? 16 : 1];  // ZOH: B_bar / B and its A-derivative per step
       float pj[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) pj[j] = 0.0f;
-      if constexpr (KEEP_A) {
+      {
         float h = hs_s[0];
         const float* brow = Bt + g * TS + 16 * s;
         const float* crow = Ct + g * TS + 16 * s;
@@ -327,14 +323,13 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
           pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
         });
       }
-      float ykeep = 0.0f;
-      if constexpr (KEEP_A) ykeep = row_transpose_sum(pj) + Dd * uu_s;  // y now: pj is not held through the sweep
+      const float ykeep = row_transpose_sum(pj) + Dd * uu_s;  // y now: pj is not held through the sweep
       float dy = go_s, sg = 0.0f;
       dzg_s = 0.0f;
       if (has_z) {
         sg = logistic_(zz_s);
         dy = go_s * (zz_s * sg);
-        if constexpr (KEEP_A) dzg_s = go_s * ykeep * (sg * __builtin_fmaf(zz_s, 1.0f - sg, 1.0f));
+        dzg_s = go_s * ykeep * (sg * __builtin_fmaf(zz_s, 1.0f - sg, 1.0f));
       }
 
       // backwards through the sub-block
@@ -346,30 +341,6 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
       for (int i = 0; i < NL; ++i) {
         const float* brow = Bt + (g + 16 * i) * TS + 16 * s;
         const float* crow = Ct + (g + 16 * i) * TS + 16 * s;
-        if constexpr (!KEEP_A) {
-          // recompute this slice's states (and its part of y); the empty asm orders the slices
-          // one after another so the compiler does not interleave them and run out of registers
-          float dts = dt_s, xus = xu_s;
-          asm volatile("" : "+v"(dts), "+v"(xus) : "v"(G[i > 0 ? i - 1 : 0]) : "memory");
-          float h = hs_s[i];
-          static_for<0, 16>([&](auto j_) {
-            constexpr int j = decltype(j_)::value;
-            const float dj = row_bcast<j>(dts);
-            const float a = exp2_(dj * Ap[i]);
-            if constexpr (ZOH) {
-              const float x = dj * Aln[i];
-              const float e = zoh_e(dj, x, a, Ainv[i]);
-              ev[j] = e;
-              edv[j] = zoh_e_dA(dj, x, a, e, Ainv[i]);
-              h = __builtin_fmaf(a, h, e * (row_bcast<j>(xus) * brow[j]));
-            } else {
-              h = __builtin_fmaf(a, h, bbar_u(dj, row_bcast<j>(xus), brow[j], a, i));
-            }
-            av[j] = a;
-            hv[j] = h;
-            pj[j] = __builtin_fmaf(crow[j], h, pj[j]);
-          });
-        }
         float Gi = G[i], dAi = dAacc[i];
         float xo = 0.0f, yo = 0.0f;  // dB, dC contributions of the odd step of a pair
         static_for<0, 16>([&](auto k_) {
@@ -412,10 +383,6 @@ __global__ __launch_bounds__(256, (NL == 1 && !ZOH) ? 3 : 2) void scan_bwd_kerne
         });
         G[i] = Gi;
         dAacc[i] = dAi;
-      }
-      if constexpr (!KEEP_A) {
-        const float y = row_transpose_sum(pj) + Dd * uu_s;  // this lane's step, before the gate
-        if (has_z) dzg_s = go_s * y * (sg * __builtin_fmaf(zz_s, 1.0f - sg, 1.0f));
       }
       const float S1 = row_transpose_sum(s1);
       const float S2 = row_transpose_sum(s2);
@@ -505,15 +472,9 @@ void go_bwd_flags(const BwdParams& p, hipStream_t s) {
 
 template <bool ZOH>
 hipError_t go_bwd_all(const BwdParams& p, bool bf16, hipStream_t s) {
-  if (bf16) {
-    if (p.N <= 16) go_bwd_flags<bf16_t, 1, ZOH>(p, s);
-    else if (p.N <= 32) go_bwd_flags<bf16_t, 2, ZOH>(p, s);
-    else go_bwd_flags<bf16_t, 4, ZOH>(p, s);
-  } else {
-    if (p.N <= 16) go_bwd_flags<float, 1, ZOH>(p, s);
-    else if (p.N <= 32) go_bwd_flags<float, 2, ZOH>(p, s);
-    else go_bwd_flags<float, 4, ZOH>(p, s);
-  }
+  // up to 16 states (one slice per lane); more states go to chunk_bwd_kernel
+  if (bf16) go_bwd_flags<bf16_t, 1, ZOH>(p, s);
+  else go_bwd_flags<float, 1, ZOH>(p, s);
   return hipGetLastError();
 }
 
