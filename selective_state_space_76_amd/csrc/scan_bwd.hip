@@ -2,7 +2,7 @@
 // discretisation (B_bar = dt B), and the fixed-order partial-sum pass shared by both
 // discretisations.  The kernels and their derivation are in scan_bwd_kernel.h; the
 // zero-order-hold variants are compiled in scan_bwd_zoh.hip.
-#include "scan_bwd_chunk.h"
+#include "scan_bwd_kernel.h"
 
 namespace ssm {
 
@@ -51,9 +51,7 @@ hipError_t launch_ckpt(const ScanParams& p, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s) {
-  if (p.zoh) return launch_bwd_zoh(p, bf16, s);
-  // more than 16 states: lanes over time (registers independent of N); up to 16: lanes over states
-  return p.N > 16 ? go_chunk_bwd_all<false>(p, bf16, s) : go_bwd_all<false>(p, bf16, s);
+  return p.zoh ? launch_bwd_zoh(p, bf16, s) : go_bwd_all<false>(p, bf16, s);
 }
 
 hipError_t launch_reduce(float* out, const float* part, int64_t count, int64_t stride, int64_t n, hipStream_t s) {
