@@ -78,6 +78,18 @@ def test_bwd_lengths(dtype, L):
     check(make(2, 20, 16, L, dtype, seed=L))
 
 
+# The kernel walks the sequence in chunks of 16 T steps (T = 8, or 16 for the default
+# discretisation above 32 states): lengths on both sides of one and several chunk edges, in
+# both directions, for each variant.
+@pytest.mark.parametrize("N,L,zoh", [(33, 256, False), (64, 257, False), (40, 511, False), (64, 767, False),
+                                     (32, 127, False), (17, 129, False), (64, 128, True), (64, 129, True),
+                                     (48, 383, True)], ids=lambda v: str(v))
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_bwd_chunk_edges(N, L, zoh, reverse):
+    print("case: bwd chunk edges N=%d L=%d zoh=%d reverse=%d f32 1x20" % (N, L, zoh, reverse), flush=True)
+    check(make(1, 20, N, L, torch.float32, seed=N + L, h0=True, dfin=True), reverse=reverse, zoh=zoh)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_bwd_optional_operands_absent(dtype):
     print("case: bwd without z, D, bias %s" % dtype, flush=True)
