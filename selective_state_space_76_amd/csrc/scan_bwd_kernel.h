@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
   __shared__ float4 cst[16 * 64];
   __shared__ float dacc[16 * 64];             // [channel][state]: dA summed over the steps done so far
   __shared__ float red[2][4][2 * CH];         // [parity][wave][dB | dC of the chunk's steps]
+  __shared__ float hck[16 * 16];              // [channel][state of the stage]: state entering the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -265,6 +266,13 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
 
     for (int64_t n0 = 0; n0 < N; n0 += 16) {
       __syncthreads();  // every wave is done with the previous stage's tile
+      // the checkpointed states entering the chunk, one (channel tid / 16, state n0 + tid % 16) per
+      // thread, loaded with the tile so that no state waits on a global load
+      float hcv = 0.0f;
+      {
+        const int64_t dh = (int64_t)cb * 16 + (tid >> 4), nh = n0 + (tid & 15);
+        if (dh < Dm && nh < N) hcv = p.ckpt[((b * nbk + c0 / 64) * Dm + dh) * N + nh];
+      }
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
         const int q = tid + 256 * k;
@@ -285,6 +293,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
           bc[((tt * 16 + nl) * KG + (s0 + e) / 4) * 16 + gl] = v;
         }
       }
+      hck[tid] = hcv;
       __syncthreads();
 
       const int ng = (N - n0) < 16 ? (int)(N - n0) : 16;
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         const int64_t n = n0 + nl;
         const float4 c4 = cs[n];
         const float A2 = c4.x, Aln = c4.y, Ai = c4.z, Gc = c4.w;
-        const float hc = p.ckpt[((b * nbk + c0 / 64) * Dm + dd) * N + n];  // state entering the chunk
+        const float hc = hck[cl * 16 + nl];  // state entering the chunk
         const f32x4* bq = bc + (nl * KG) * 16 + g;
         const f32x4* cq = bc + ((16 + nl) * KG) * 16 + g;
 
@@ -339,14 +348,15 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         }
 
         // adjoint: the lane's steps folded from its last, as if nothing entered from the right
-        float QG = 0.0f;
+        float QG = 0.0f, dc[T];
 #pragma unroll
         for (int k = KG - 1; k >= 0; --k) {
           const f32x4 cv = cq[k * 16];
 #pragma unroll
           for (int e = 3; e >= 0; --e) {
             const int s = 4 * k + e;
-            QG = (s == T - 1) ? dy[s] * cv[e] : __builtin_fmaf(a[s + 1 < T ? s + 1 : 0], QG, dy[s] * cv[e]);
+            dc[s] = dy[s] * cv[e];
+            QG = (s == T - 1) ? dc[s] : __builtin_fmaf(a[s + 1 < T ? s + 1 : 0], QG, dc[s]);
           }
         }
         float Qr = a[0] * QG, Pr = Pl;  // adjoint this lane passes to its left neighbour: Qr + Pr X_in
@@ -362,13 +372,11 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         float* rw = red[par][w];
 #pragma unroll
         for (int k = KG - 1; k >= 0; --k) {
-          const f32x4 cv = cq[k * 16];
           const f32x4 bv = bq[k * 16];
 #pragma unroll
           for (int e = 3; e >= 0; --e) {
             const int s = 4 * k + e;
-            G = (s == T - 1) ? __builtin_fmaf(dy[s], cv[e], G)
-                             : __builtin_fmaf(a[s + 1 < T ? s + 1 : 0], G, dy[s] * cv[e]);
+            G = (s == T - 1) ? G + dc[s] : __builtin_fmaf(a[s + 1 < T ? s + 1 : 0], G, dc[s]);
             const float hp = s > 0 ? h[s > 0 ? s - 1 : 0] : hs;
             const float tt = G * hp * a[s];
             float vb;  // dB term
@@ -399,9 +407,11 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
           }
         }
 
-        // dA over the row's lanes, added in lane order of the butterfly (fixed)
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) dAl += __shfl_xor(dAl, off, 16);
+        // dA over the row's lanes: rotations by 8, 4, 2, 1 within the row (a fixed order; lane 0 keeps it)
+        dAl += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dAl), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+        dAl += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dAl), 0x124 /* row_ror:4 */, 0xf, 0xf, false));
+        dAl += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dAl), 0x122 /* row_ror:2 */, 0xf, 0xf, false));
+        dAl += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dAl), 0x121 /* row_ror:1 */, 0xf, 0xf, false));
         if (g == 0) da[n] += dAl;
 
         // dB, dC over the workgroup's 16 channels: the 4 waves' row sums through LDS, in wave order
