@@ -111,6 +111,14 @@ def _expect(t, shape, dtype, name, device=None):
         raise ValueError("%s: expected a tensor on %s, got %s" % (name, device, t.device))
 
 
+def _nonempty(**sizes):
+    """The library computes nothing for an empty tensor and refuses one (SSM_ERR_SHAPE); say so
+    here, by name, rather than pass on an empty tensor's null data pointer."""
+    bad = ", ".join("%s=%d" % kv for kv in sizes.items() if kv[1] < 1)
+    if bad:
+        raise ValueError("empty input: every size must be at least 1 (%s)" % bad)
+
+
 def _stream(stream, device):
     """The caller's stream, by default the current stream of the tensors' device."""
     if stream is None:
@@ -140,6 +148,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     lib = load()
     Bsz, Dm, L = u.shape
     N = A.shape[1]
+    _nonempty(batch=Bsz, dim=Dm, dstate=N, seqlen=L)
     io = _io_dtype(u)
     device = u.device
     sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
@@ -182,6 +191,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     lib = load()
     Bsz, Dm = u.shape
     N = A.shape[1]
+    _nonempty(batch=Bsz, dim=Dm, dstate=N)
     io = _io_dtype(u)
     device = u.device
     if out is None:
@@ -212,6 +222,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     lib = load()
     Bsz, Dm, L = u.shape
     N = A.shape[1]
+    _nonempty(batch=Bsz, dim=Dm, dstate=N, seqlen=L)
     io = _io_dtype(u)
     device = u.device
     sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
@@ -257,6 +268,7 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_stat
     lib = load()
     Bsz, Dm, L = x.shape
     K = weight.shape[1]
+    _nonempty(batch=Bsz, dim=Dm, seqlen=L, width=K)
     io = _io_dtype(x)
     device = x.device
     if out is None:
@@ -282,6 +294,7 @@ def conv1d_update(conv_state, x, weight, bias=None, *, out=None, stream=None):
     lib = load()
     Bsz, Dm = x.shape
     K = weight.shape[1]
+    _nonempty(batch=Bsz, dim=Dm, width=K)
     io = _io_dtype(x)
     device = x.device
     if out is None:
