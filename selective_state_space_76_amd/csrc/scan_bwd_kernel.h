@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         const f32x4* cq = bc + ((16 + nl) * KG) * 16 + g;
 
         // forward through the chunk
-        float a[T], h[T];
+        float a[T], h[T], ezs[ZOH ? T : 1];  // ezs: the ZOH factor of each step, reused by the adjoint
         float Qa = 0.0f, Qb = 0.0f;
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
@@ -316,7 +316,8 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
           for (int e = 0; e < 4; ++e) {
             const int s = 4 * k + e;
             a[s] = exp2_(dt[s] * A2);
-            const float bb = ZOH ? zoh_e(dt[s], dt[s] * Aln, a[s], Ai) * (xu[s] * bv[e]) : xu[s] * bv[e];
+            if constexpr (ZOH) ezs[s] = zoh_e(dt[s], dt[s] * Aln, a[s], Ai);
+            const float bb = ZOH ? ezs[ZOH ? s : 0] * (xu[s] * bv[e]) : xu[s] * bv[e];
             h[s] = bb;  // B_bar u for now; the rerun turns it into the state
             if (s < T / 2) Qa = __builtin_fmaf(a[s], Qa, bb);
             else Qb = __builtin_fmaf(a[s], Qb, bb);
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
             float vb;  // dB term
             if constexpr (ZOH) {
               const float x = dt[s] * Aln;
-              const float ez = zoh_e(dt[s], x, a[s], Ai);
+              const float ez = ezs[ZOH ? s : 0];
               const float gb = G * bv[e];
               const float gbu = gb * uu[s];
               S1[s] = __builtin_fmaf(gb, ez, S1[s]);
