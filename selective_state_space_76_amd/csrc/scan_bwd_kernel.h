@@ -188,7 +188,9 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
   const int r = lane >> 4, g = lane & 15;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int cb = logical % p.nblk;
-  const int64_t b = logical / p.nblk;
+  const int rest = logical / p.nblk;
+  const int seg = rest % p.S;               // segment of the sequence (one when it is not split)
+  const int64_t b = rest / p.S;
   const int64_t L = p.L, N = p.N, Dm = p.Dm;
   const int64_t nbk = (L + 63) / 64;
   const int cl = w * 4 + r;
@@ -206,7 +208,11 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
     const int64_t n = g + 16 * k;
     if (n < N) {
       const float a = p.A[dd * N + n];
-      const float gf = (dval && p.dfinal) ? p.dfinal[(b * Dm + d) * N + n] : 0.0f;
+      // adjoint entering the segment's last step from the right: the final-state gradient, or
+      // for a split sequence the composition of the segments to the right
+      const float gf = !dval ? 0.0f
+                             : p.adj_in ? p.adj_in[(((int64_t)seg * p.Bsz + b) * Dm + d) * N + n]
+                                        : (p.dfinal ? p.dfinal[(b * Dm + d) * N + n] : 0.0f);
       cs[n] = make_float4(a * kLog2e, a, ZOH ? 1.0f / a : 0.0f, gf);
       da[n] = 0.0f;
     }
@@ -221,10 +227,13 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
   IO* dz_row = has_z ? reinterpret_cast<IO*>(p.dz) + (b * Dm + dd) * L : nullptr;
   float dDacc = 0.0f, dbacc = 0.0f;  // this lane's dD and dbias terms
   int par = 0;                       // parity of the dB/dC exchange buffer
-  const int64_t nch = (L + CH - 1) / CH;
+  // the segment's chunks (a split segment is a whole number of chunks; the last one may be ragged)
+  const int64_t tb = (int64_t)seg * p.seg_len;
+  const int64_t te = (tb + p.seg_len < L) ? tb + p.seg_len : L;
+  const int64_t nch = (te - tb + CH - 1) / CH;
 
   for (int64_t ci = nch - 1; ci >= 0; --ci) {
-    const int64_t c0 = ci * CH;
+    const int64_t c0 = tb + ci * CH;
     const int64_t t0 = c0 + g * T;
 
     // per-(channel, step) values of this lane's 16 steps
@@ -460,8 +469,8 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
     for (int k = 0; k < 4; ++k) {
       const int64_t n = g + 16 * k;
       if (n < N) {
-        p.part_a[(b * Dm + d) * N + n] = da[n];
-        if (p.dh0) p.dh0[(b * Dm + d) * N + n] = cs[n].w;
+        p.part_a[(((int64_t)seg * p.Bsz + b) * Dm + d) * N + n] = da[n];
+        if (p.dh0 && seg == 0) p.dh0[(b * Dm + d) * N + n] = cs[n].w;
       }
     }
   }
@@ -471,15 +480,16 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
     dbacc += __shfl_xor(dbacc, off, 16);
   }
   if (dval && g == 0) {
-    p.part_d[b * Dm + d] = dDacc;
-    p.part_d[p.Bsz * Dm + b * Dm + d] = dbacc;
+    const int64_t SB = (int64_t)p.S * p.Bsz;
+    p.part_d[((int64_t)seg * p.Bsz + b) * Dm + d] = dDacc;
+    p.part_d[SB * Dm + ((int64_t)seg * p.Bsz + b) * Dm + d] = dbacc;
   }
 }
 
 
 template <typename IO, int T, bool ZOH, bool REV, bool VEC>
 void go_bwd(const BwdParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((scan_bwd_kernel<IO, T, ZOH, REV, VEC>), dim3((unsigned)(p.Bsz * p.nblk)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<IO, T, ZOH, REV, VEC>), dim3((unsigned)(p.Bsz * p.nblk * p.S)), dim3(256), 0, s, p);
 }
 
 template <typename IO, int T, bool ZOH>
@@ -515,7 +525,7 @@ hipError_t go_bwd_all(const BwdParams& p, bool bf16, hipStream_t s) {
 // the checkpoint pass (the scan kernel's mode 2) for one discretisation
 template <typename IO, int NL, bool ZOH, bool REV, bool VEC>
 void go_ckpt(const ScanParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((scan_kernel<IO, NL, 2, ZOH, REV, VEC>), dim3((unsigned)(p.Bsz * p.nblk)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((scan_kernel<IO, NL, 2, ZOH, REV, VEC>), dim3((unsigned)(p.Bsz * p.nblk * p.S)), dim3(256), 0, s, p);
 }
 
 template <typename IO, int NL, bool ZOH>

@@ -83,24 +83,57 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
 ssm_status launch_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH; }
 
 struct BwdPlan {
-  int64_t nblk = 0, nbk = 0;
-  size_t ckpt = 0, bc = 0, a = 0, d = 0, total = 0;
+  int64_t nblk = 0, nbk = 0, S = 1, seg_len = 0;
+  size_t ckpt = 0, bc = 0, a = 0, d = 0;
+  size_t seg_state = 0, seg_dsum = 0, carries = 0, adj_q = 0, adj_dsum = 0, adj_in = 0, total = 0;
 };
 
+constexpr int kBwdTargetBlocks = 768;  // 3 backward workgroups per CU on 256 CUs
+
+// Shape-only, like the forward's plan.  Few channels and a long sequence: split the sequence
+// into segments (whole 256-step chunks, >= 1024 steps) so that about kBwdTargetBlocks
+// workgroups run; each segment's checkpoints start from a carried state (summary pass + carry)
+// and its adjoint from a carried adjoint (adjoint summary + carry).
 bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl) {
   Plan fp;
   if (!make_plan(s, &fp)) return false;  // same size limits as the forward
   const int64_t Bsz = s->batch, Dm = s->dim, N = s->dstate, L = s->seqlen;
   pl->nblk = (Dm + 15) / 16;
   pl->nbk = (L + 63) / 64;
+  const int64_t base = Bsz * pl->nblk;
+  pl->S = 1;
+  pl->seg_len = ((L + 255) / 256) * 256;
+  if (base < kBwdTargetBlocks / 2 && L >= 2 * kMinSegment) {
+    const int64_t want = (kBwdTargetBlocks + base - 1) / base;
+    int64_t seg = (L + want - 1) / want;
+    seg = ((seg + 255) / 256) * 256;
+    if (seg < kMinSegment) seg = kMinSegment;
+    const int64_t S = (L + seg - 1) / seg;
+    if (S > 1) {
+      pl->S = S;
+      pl->seg_len = seg;
+    }
+  }
+  if (base * pl->S > (int64_t(1) << 31) - 1) return false;
+  const int64_t BD = Bsz * Dm, BDN = BD * N;
   int64_t x;
-  if (!mul_ok(Bsz * Dm * N, pl->nbk, &x)) return false;
+  if (!mul_ok(BDN, pl->nbk, &x)) return false;
   pl->ckpt = round256(sizeof(float) * (size_t)x);
   if (!mul_ok(2 * pl->nblk * Bsz * N, L, &x)) return false;
   pl->bc = round256(sizeof(float) * (size_t)x);
-  pl->a = round256(sizeof(float) * (size_t)(Bsz * Dm * N));
-  pl->d = round256(sizeof(float) * (size_t)(2 * Bsz * Dm));
-  pl->total = pl->ckpt + pl->bc + pl->a + pl->d;
+  if (!mul_ok(BDN, pl->S, &x)) return false;
+  pl->a = round256(sizeof(float) * (size_t)x);
+  pl->d = round256(sizeof(float) * (size_t)(2 * pl->S * BD));
+  if (pl->S > 1) {
+    pl->seg_state = round256(sizeof(float) * (size_t)((pl->S - 1) * BDN));
+    pl->seg_dsum = round256(sizeof(float) * (size_t)((pl->S - 1) * BD));
+    pl->carries = round256(sizeof(float) * (size_t)(pl->S * BDN));
+    pl->adj_q = pl->carries;
+    pl->adj_dsum = round256(sizeof(float) * (size_t)(pl->S * BD));
+    pl->adj_in = pl->carries;
+  }
+  pl->total = pl->ckpt + pl->bc + pl->a + pl->d + pl->seg_state + pl->seg_dsum + pl->carries + pl->adj_q +
+              pl->adj_dsum + pl->adj_in;
   return true;
 }
 
@@ -289,26 +322,48 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   const bool bf16 = shape->io_dtype == SSM_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* ckpt = reinterpret_cast<float*>(ws);
-  float* part_bc = reinterpret_cast<float*>(ws + pl.ckpt);
-  float* part_a = reinterpret_cast<float*>(ws + pl.ckpt + pl.bc);
-  float* part_d = reinterpret_cast<float*>(ws + pl.ckpt + pl.bc + pl.a);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { float* q = reinterpret_cast<float*>(ws + off); off += bytes; return q; };
+  float* ckpt = take(pl.ckpt);
+  float* part_bc = take(pl.bc);
+  float* part_a = take(pl.a);
+  float* part_d = take(pl.d);
+  float* seg_state = take(pl.seg_state);
+  float* seg_dsum = take(pl.seg_dsum);
+  float* carries = take(pl.carries);
+  float* adj_q = take(pl.adj_q);
+  float* adj_dsum = take(pl.adj_dsum);
+  float* adj_in = take(pl.adj_in);
   const int vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;
   const int rev = (shape->flags & SSM_FLAG_REVERSE) ? 1 : 0;
   const int zoh = (shape->flags & SSM_FLAG_ZOH) ? 1 : 0;
+  const bool split = pl.S > 1;
+  const int64_t SB = pl.S * Bsz;
 
+  // checkpoints: the state entering every 64-step block (a split sequence: each segment from
+  // its carry, as in the forward's split)
   ssm::ScanParams fp;
   memset(&fp, 0, sizeof(fp));
   fp.u = u; fp.delta = delta; fp.A = A; fp.B = B; fp.C = C; fp.bias = delta_bias; fp.init = initial_state;
   fp.ckpt = ckpt;
   fp.Bsz = Bsz; fp.Dm = Dm; fp.N = N; fp.L = L;
-  fp.S = 1;
-  fp.seg_len = pl.nbk * 64;
+  fp.S = (int)pl.S;
+  fp.seg_len = split ? pl.seg_len : pl.nbk * 64;
   fp.nblk = (int)pl.nblk;
   fp.vec = vec;
   fp.reverse = rev;
   fp.zoh = zoh;
-  ssm_status rc = launch_status(ssm::launch_ckpt(fp, bf16, st));
+  ssm_status rc;
+  if (split) {
+    fp.seg_state = seg_state;
+    fp.seg_dsum = seg_dsum;
+    rc = launch_status(ssm::launch_scan(fp, bf16, 1, st));
+    if (rc != SSM_OK) return rc;
+    fp.carries = carries;
+    rc = launch_status(ssm::launch_carry(fp, st));
+    if (rc != SSM_OK) return rc;
+  }
+  rc = launch_status(ssm::launch_ckpt(fp, bf16, st));
   if (rc != SSM_OK) return rc;
 
   ssm::BwdParams bp;
@@ -318,10 +373,21 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   bp.du = du; bp.ddelta = ddelta; bp.dz = dz; bp.dh0 = dinitial_state;
   bp.part_bc = part_bc; bp.part_a = part_a; bp.part_d = part_d;
   bp.Bsz = Bsz; bp.Dm = Dm; bp.N = N; bp.L = L;
+  bp.S = (int)pl.S;
+  bp.seg_len = pl.seg_len;
   bp.nblk = (int)pl.nblk;
   bp.vec = vec;
   bp.reverse = rev;
   bp.zoh = zoh;
+  if (split) {  // the adjoint entering each segment from the right
+    bp.adj_q = adj_q;
+    bp.adj_dsum = adj_dsum;
+    rc = launch_status(ssm::launch_adj_summary(bp, bf16, st));
+    if (rc != SSM_OK) return rc;
+    rc = launch_status(ssm::launch_adj_carry(bp, adj_in, st));
+    if (rc != SSM_OK) return rc;
+    bp.adj_in = adj_in;
+  }
   rc = launch_status(ssm::launch_bwd(bp, bf16, st));
   if (rc != SSM_OK) return rc;
 
@@ -329,13 +395,13 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   if (rc != SSM_OK) return rc;
   rc = launch_status(ssm::launch_reduce(dC, part_bc + pl.nblk * BNL, pl.nblk, BNL, BNL, st));
   if (rc != SSM_OK) return rc;
-  rc = launch_status(ssm::launch_reduce(dA, part_a, Bsz, Dm * N, Dm * N, st));
+  rc = launch_status(ssm::launch_reduce(dA, part_a, SB, Dm * N, Dm * N, st));
   if (rc != SSM_OK) return rc;
   if (dD) {
-    rc = launch_status(ssm::launch_reduce(dD, part_d, Bsz, Dm, Dm, st));
+    rc = launch_status(ssm::launch_reduce(dD, part_d, SB, Dm, Dm, st));
     if (rc != SSM_OK) return rc;
   }
-  if (ddelta_bias) rc = launch_status(ssm::launch_reduce(ddelta_bias, part_d + Bsz * Dm, Bsz, Dm, Dm, st));
+  if (ddelta_bias) rc = launch_status(ssm::launch_reduce(ddelta_bias, part_d + SB * Dm, SB, Dm, Dm, st));
   return rc;
 }
 

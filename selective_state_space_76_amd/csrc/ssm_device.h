@@ -179,8 +179,8 @@ __device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
 
 // MODE 0: output pass (writes out and, for the last segment, final_state).
 // MODE 1: summary pass over segments 0..S-2 (writes seg_state and seg_dsum).
-// MODE 2: checkpoint pass for the backward (one segment; writes the state
-//         entering every 64-step block to ckpt).
+// MODE 2: checkpoint pass for the backward (writes the state entering every
+//         64-step block to ckpt; a split sequence starts each segment from its carry).
 // REV: logical step t reads physical position L-1-t.  VEC: rows allow 16-byte
 // vector loads (L a multiple of 8 for bf16, of 4 for fp32, and L >= 8).
 //
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
     Ainv[i] = ZOH ? 1.0f / Aln[i] : 0.0f;
     float h0 = 0.0f;
     if (MODE != 1) {
-      if (MODE == 0 && p.carries) h0 = p.carries[(((int64_t)seg * p.Bsz + b) * Dm + dd) * N + nn];
+      if (p.carries) h0 = p.carries[(((int64_t)seg * p.Bsz + b) * Dm + dd) * N + nn];
       else if (p.init) h0 = p.init[(b * Dm + dd) * N + nn];
     }
     h[i] = nv ? h0 : 0.0f;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
       const int64_t nbk = (L + 63) / 64;
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if (g + 16 * i < N) p.ckpt[((b * nbk + blk) * Dm + d) * N + g + 16 * i] = h[i];
+        if (g + 16 * i < N) p.ckpt[((b * nbk + t0 / 64) * Dm + d) * N + g + 16 * i] = h[i];
     }
     const float* Bt = tile;
     const float* Ct = tile + (MODE == 0 ? NP * TS : 0);

@@ -64,9 +64,14 @@ struct BwdParams {
   void* dz;               // [B,D,L], written when z is given
   float* dh0;             // [B,D,N] gradient of the initial state, or null
   float* part_bc;         // [2,nblk,B,N,L] dB and dC summed over each workgroup's 16 channels
-  float* part_a;          // [B,D,N] dA summed over steps, per batch row
-  float* part_d;          // [2,B,D] dD and dbias summed over steps, per batch row
+  float* part_a;          // [S,B,D,N] dA summed over a segment's steps, per batch row
+  float* part_d;          // [2,S,B,D] dD and dbias summed over a segment's steps, per batch row
+  const float* adj_in;    // [S,B,D,N] adjoint entering each segment from the right (split runs), or null
+  float* adj_q;           // [S,B,D,N] adjoint summary of each segment s >= 1 (split runs)
+  float* adj_dsum;        // [S,B,D] sum of the step sizes of each segment s >= 1 (split runs)
   int64_t Bsz, Dm, N, L;
+  int64_t seg_len;        // steps per segment, a multiple of 256 when S > 1
+  int S;                  // number of segments (1: no split)
   int nblk;               // channel blocks of 16
   int vec;                // rows allow 16-byte vector loads
   int reverse;
@@ -94,6 +99,10 @@ hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
 // the zero-order-hold variants of the two (p.zoh set), compiled separately
 hipError_t launch_ckpt_zoh(const ScanParams& p, bool bf16, hipStream_t s);
 hipError_t launch_bwd_zoh(const BwdParams& p, bool bf16, hipStream_t s);
+// sequence split of the backward: the adjoint summary of segments 1..S-1 (adj_q, adj_dsum), then
+// the adjoint entering each segment (adj_in), composed from the right
+hipError_t launch_adj_summary(const BwdParams& p, bool bf16, hipStream_t s);
+hipError_t launch_adj_carry(const BwdParams& p, float* adj_in, hipStream_t s);
 // out[i] = sum_k part[k * stride + i] for i < n, k < count (k ascending)
 hipError_t launch_reduce(float* out, const float* part, int64_t count, int64_t stride, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);

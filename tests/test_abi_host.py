@@ -114,6 +114,24 @@ def test_workspace_size_formula():
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn)
 
 
+def test_bwd_workspace_size_split():
+    # few channels, long sequence: the backward splits the sequence into segments of whole
+    # 256-step chunks (>= 1024 steps) and adds the split's carries and adjoint summaries
+    lib = L.load()
+    s = shp(batch=1, dim=20, dstate=16, seqlen=5000)
+    S, nblk, nbk = 5, 2, (5000 + 63) // 64   # 2 workgroups of channels -> 5 segments of 1024 (last 904)
+    bdn, bd = 20 * 16, 20
+    r = lambda x: (x + 255) // 256 * 256
+    want = (r(4 * bdn * nbk) + r(4 * 2 * nblk * 16 * 5000) + r(4 * S * bdn) + r(4 * 2 * S * bd)
+            + r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + 3 * r(4 * S * bdn) + r(4 * S * bd))
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) == want
+    # enough channels: no split, the plain layout
+    s = shp(batch=8, dim=1536, dstate=16, seqlen=2048)
+    nblk, nbk, bdn = 96, 32, 8 * 1536 * 16
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) == (
+        r(4 * bdn * nbk) + r(4 * 2 * nblk * 8 * 16 * 2048) + r(4 * bdn) + r(4 * 2 * 8 * 1536))
+
+
 def step(batch=4, dim=8, dstate=16, io=L.SSM_BF16, flags=0, **kw):
     lib = L.load()
     p = dict(state=fake(1), u=fake(2), delta=fake(3), A=fake(4), B=fake(5), C=fake(6), D=None, z=None,

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from selective_state_space_76_amd import scan_bwd
+from selective_state_space_76_amd import SSM_F32, bwd_workspace_size, scan_bwd
 from selective_state_space_76_amd import workloads as W
 from tests.gpu_util import rel_err, tol_for
 
@@ -88,6 +88,28 @@ def test_bwd_lengths(dtype, L):
 def test_bwd_chunk_edges(N, L, zoh, reverse):
     print("case: bwd chunk edges N=%d L=%d zoh=%d reverse=%d f32 1x20" % (N, L, zoh, reverse), flush=True)
     check(make(1, 20, N, L, torch.float32, seed=N + L, h0=True, dfin=True), reverse=reverse, zoh=zoh)
+
+
+# Few channels and a long sequence: the backward splits the sequence into segments (checkpoints
+# from carried states, adjoints from carried adjoint summaries).  1 x 20 x N x 5000 runs 5
+# segments of 1024 steps (the last 904); 2 x 8 x N x 2348 runs 3 (the last 300).
+@pytest.mark.parametrize("Bsz,Dm,L", [(1, 20, 5000), (2, 8, 2348)], ids=["5seg", "3seg"])
+@pytest.mark.parametrize("N,zoh", [(16, False), (64, False), (16, True), (40, True)], ids=lambda v: str(v))
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_bwd_sequence_split(Bsz, Dm, L, N, zoh, reverse):
+    print("case: bwd split %dx%dx%dx%d zoh=%d reverse=%d f32" % (Bsz, Dm, N, L, zoh, reverse), flush=True)
+    r = lambda x: (x + 255) // 256 * 256
+    nblk, bdn = (Dm + 15) // 16, Bsz * Dm * N
+    unsplit = r(4 * bdn * ((L + 63) // 64)) + r(8 * nblk * Bsz * N * L) + r(4 * bdn) + r(8 * Bsz * Dm)
+    assert bwd_workspace_size(Bsz, Dm, N, L, SSM_F32) > unsplit  # the split plan is the one taken
+    check(make(Bsz, Dm, N, L, torch.float32, seed=7 * N + L, h0=True, dfin=True), reverse=reverse, zoh=zoh)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 64])
+def test_bwd_sequence_split_dtypes(dtype, N):
+    print("case: bwd split 1x24x%dx4100 %s" % (N, dtype), flush=True)
+    check(make(1, 24, N, 4100, dtype, seed=N + 3, gate=(N == 16), bias=(N == 16), h0=True, dfin=True))
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
