@@ -135,8 +135,13 @@ ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t 
 
 /* Bytes of device workspace ssm_scan_bwd needs for this shape (0 for an invalid
  * shape): block checkpoints of the state, B*D*ceil(L/64)*N fp32; per-workgroup
- * partial sums of dB and dC, 2*ceil(D/16)*B*N*L fp32; and the per-batch-row
- * partial sums of dA, dD and ddelta_bias. */
+ * partial sums of dB and dC, 2*ceil(D/16)*B*N*L fp32; and the per-(segment,
+ * batch row) partial sums of dA, dD and ddelta_bias.  When the shape has few
+ * channels and a long sequence (fewer than 384 blocks of 16 channels over the batch
+ * and L >= 2048) the sequence is split into S segments, as in the forward: then
+ * also the carried states of the checkpoints and, per segment, the summary and the
+ * carried value of the adjoint (O(S*B*D*N) fp32).  The choice depends on the shape
+ * only. */
 size_t ssm_scan_bwd_workspace_size(const ssm_shape* shape);
 
 /* Gradients of ssm_scan_fwd (training backward pass).  The pages describe only the
