@@ -22,7 +22,8 @@
 //     (channel, step) value is computed once, not once per state.
 //   * Per state update: one multiply for the exp2 argument, v_exp_f32, one
 //     multiply for B_bar*u, one FMA for h and one FMA for C*h.  The sum over
-//     n of C*h is a 16 x 16 transpose through LDS (wave-local, no barrier).
+//     n of C*h is a reduce-scatter of the 16 x 16 (state x step) tile in
+//     registers with DPP adds (row_transpose_sum); lane g ends with step g.
 //   * Sequences with too few channels to fill the chip are cut into S
 //     segments: a summary pass scans each segment from a zero state and keeps
 //     its end state and the sum of its step sizes, a carry pass chains the
