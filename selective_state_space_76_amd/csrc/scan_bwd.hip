@@ -50,13 +50,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(float* out, const float* pa
 // recurrence G_t = dy_t C_t + A_bar_{t+1} G_{t+1} does not involve the state, so what a segment
 // passes to its left neighbour is affine in the adjoint X entering it from the right: P X + Q,
 // with P = exp(A * (sum of the segment's step sizes)).  This kernel computes Q (X = 0) with the
-// backward kernel's layout (rows = channels, lanes = 8 consecutive steps of a 128-step chunk,
+// backward kernel's layout (rows = channels, lanes = 16 consecutive steps of a 256-step chunk,
 // states in a loop, chunks from last to first) and the segment's step-size sum (Kahan per lane,
 // lanes added in a fixed order); adj_carry_kernel composes the segments from the right.
 template <typename IO, bool REV, bool VEC>
 __global__ __launch_bounds__(256) void adj_summary_kernel(BwdParams p) {
   using namespace bwdc;
-  constexpr int T = 8;
+  constexpr int T = 16;                       // steps per lane (a split segment is whole 256-step chunks)
   constexpr int CH = 16 * T;                  // steps per chunk
   constexpr int KG = T / 4;                   // float4 groups per lane
   constexpr int EPC = 16 / (int)sizeof(IO);   // elements per 16-byte piece
