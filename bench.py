@@ -245,19 +245,20 @@ def bench_bwd(args, torch, ssm, W):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     grads = None
 
-    def call(x, zoh=False):
+    def call(x, zoh=False, saved=False):
         nonlocal grads
         grads = ssm.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                             dout=x["dout"], grads=grads, workspace=ws, zoh=zoh)
+                             dout=x["dout"], grads=grads, workspace=ws, zoh=zoh,
+                             checkpoints=x["ck"] if saved else None)
 
-    def timed(n, zoh):
+    def timed(n, zoh, saved=False):
         for k in range(max(2, args.warmup)):
-            call(sets[k % R], zoh)
+            call(sets[k % R], zoh, saved)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
         torch.cuda.synchronize()
         for k in range(n):
             ev[2 * k].record()
-            call(sets[k % R], zoh)
+            call(sets[k % R], zoh, saved)
             ev[2 * k + 1].record()
         torch.cuda.synchronize()
         return sorted(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n))
@@ -266,11 +267,19 @@ def bench_bwd(args, torch, ssm, W):
     ms = timed(n, False)
     mean = sum(ms) / n
     mz = timed(5, True)  # the zero-order-hold variant, same inputs (context, not the bench value)
+    # context: the backward from the checkpoints a saving forward wrote (ssm_scan_bwd_saved), as a
+    # training step runs it; the forward that wrote them is outside the timed calls
+    for x in sets:
+        x["ck"] = torch.empty(ssm.checkpoints_shape(w.batch, w.dim, w.dstate, w.seqlen), device="cuda")
+        ssm.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                     checkpoints=x["ck"])
+    msv = timed(n, False, saved=True)
     b = bwd_bytes(w)
     return {"workload": w.name, "rotated_input_sets": R, "call_ms": mean, "call_ms_median": ms[n // 2],
             "value": w.updates / (mean * 1e-3), "unit": "state-updates/s",
             "workspace_bytes": need, "algorithmic_bytes_per_call": b,
-            "hbm_GBs": b / (mean * 1e-3) / 1e9, "zoh_call_ms": sum(mz) / len(mz)}
+            "hbm_GBs": b / (mean * 1e-3) / 1e9, "zoh_call_ms": sum(mz) / len(mz),
+            "from_saved_checkpoints_call_ms": sum(msv) / len(msv)}
 
 
 def conv_bytes(w, K) -> int:
@@ -513,7 +522,8 @@ def main():
         d["roofline"]["frac_of_copy_peak"] = d["roofline"]["achieved"] / cp
     if not args.no_bwd:
         bw = bench_bwd(args, torch, ssm, W)
-        log("backward: %.4f ms/call -> %.3e updates/s" % (bw["call_ms"], bw["value"]))
+        log("backward: %.4f ms/call -> %.3e updates/s (from saved checkpoints %.4f ms, ZOH %.4f ms)"
+            % (bw["call_ms"], bw["value"], bw["from_saved_checkpoints_call_ms"], bw["zoh_call_ms"]))
         res["backward"] = bw
     if not args.no_conv:
         pre, dec = bench_conv(args, torch, ssm, W)

@@ -79,7 +79,7 @@ typedef struct ssm_shape {
 } ssm_shape;
 
 /* Version of this header's ABI (bumped on any incompatible change). */
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 int ssm_abi_version(void);
 
 /* Static string for a status code (never NULL). */
@@ -116,6 +116,21 @@ ssm_status ssm_scan_fwd(const ssm_shape* shape,
                         void* out, float* final_state,
                         void* workspace, size_t workspace_bytes,
                         struct ihipStream_t* stream);
+
+/* ssm_scan_fwd that also saves what ssm_scan_bwd_saved needs, so a training step does
+ * not recompute it:
+ *   checkpoints      : [B, ceil(L/64), D, N] fp32, written: the state entering every
+ *                      64-step block (block k starts at step 64 k in scan order).
+ *                      Required; must not overlap any other argument.
+ * Every other argument, the outputs and the errors are those of ssm_scan_fwd. */
+ssm_status ssm_scan_fwd_save(const ssm_shape* shape,
+                             const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D,
+                             const void* z, const float* delta_bias,
+                             const float* initial_state,
+                             void* out, float* final_state, float* checkpoints,
+                             void* workspace, size_t workspace_bytes,
+                             struct ihipStream_t* stream);
 
 /* One recurrent generation step (the scan body with L = 1), state updated in place:
  * the fixed-size state replaces a growing cache (fsdata.site article, section 3.2
@@ -163,8 +178,9 @@ size_t ssm_scan_bwd_workspace_size(const ssm_shape* shape);
  *   workspace        : required, at least ssm_scan_bwd_workspace_size() bytes
  * shape->flags may hold SSM_FLAG_REVERSE and SSM_FLAG_ZOH, as in the forward call
  * (under ZOH the derivatives of B_bar = (exp(dt A) - 1) / A * B with respect to dt, A,
- * B and u are taken, with the A -> 0 limit where A is zero).  No output may overlap an input, another output or the workspace.  Every sum is
- * taken in a fixed order, so results are bitwise reproducible. */
+ * B and u are taken, with the A -> 0 limit where A is zero).  No output may overlap an
+ * input, another output or the workspace.  Every sum is taken in a fixed order, so
+ * results are bitwise reproducible. */
 ssm_status ssm_scan_bwd(const ssm_shape* shape,
                         const void* u, const void* delta, const float* A,
                         const void* B, const void* C, const float* D,
@@ -175,6 +191,29 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape,
                         float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
                         void* workspace, size_t workspace_bytes,
                         struct ihipStream_t* stream);
+
+/* Bytes of device workspace ssm_scan_bwd_saved needs for this shape (0 for an invalid
+ * shape): that of ssm_scan_bwd without the checkpoints and their split. */
+size_t ssm_scan_bwd_saved_workspace_size(const ssm_shape* shape);
+
+/* ssm_scan_bwd from the checkpoints that ssm_scan_fwd_save wrote for the same inputs
+ * (same shape, flags, initial_state, A, B, delta, delta_bias and u), instead of a
+ * checkpoint pass of its own:
+ *   checkpoints      : [B, ceil(L/64), D, N] fp32, read only.  Required; must not
+ *                      overlap an output or the workspace.
+ *   workspace        : required, at least ssm_scan_bwd_saved_workspace_size() bytes
+ * Every other argument, the outputs and the errors are those of ssm_scan_bwd. */
+ssm_status ssm_scan_bwd_saved(const ssm_shape* shape,
+                              const void* u, const void* delta, const float* A,
+                              const void* B, const void* C, const float* D,
+                              const void* z, const float* delta_bias,
+                              const float* initial_state,
+                              const void* dout, const float* dfinal_state,
+                              const float* checkpoints,
+                              void* du, void* ddelta, float* dA, float* dB, float* dC,
+                              float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
+                              void* workspace, size_t workspace_bytes,
+                              struct ihipStream_t* stream);
 
 /* The step that produces u: causal depthwise conv1d over time, plus a bias, then
  * SiLU (ai.xwebgame.com Mamba page, the PyTorch block's step 2: a Conv1d with one

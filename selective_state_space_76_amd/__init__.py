@@ -12,8 +12,10 @@ The C ABI is include/ssm_scan.h; the library is libssmscan.so in this package,
 built by `python -m selective_state_space_76_amd.build`.
 """
 from ._lib import (SSMError, load, scan_fwd, state_update, conv1d_fwd, conv1d_update,  # noqa: F401
-                   scan_bwd, bwd_workspace_size, workspace_size, SSM_F32, SSM_BF16, SSM_FLAG_ZOH, SSM_FLAG_REVERSE, LIB_PATH)
+                   scan_bwd, bwd_workspace_size, workspace_size, checkpoints_shape, SSM_F32, SSM_BF16,
+                   SSM_FLAG_ZOH, SSM_FLAG_REVERSE, LIB_PATH)
 from .autograd import SelectiveScanFn, selective_scan  # noqa: F401
 
 __all__ = ["scan_fwd", "scan_bwd", "selective_scan", "SelectiveScanFn", "state_update", "conv1d_fwd",
-           "conv1d_update", "workspace_size", "bwd_workspace_size", "load", "SSMError", "LIB_PATH"]
+           "conv1d_update", "workspace_size", "bwd_workspace_size", "checkpoints_shape", "load", "SSMError",
+           "LIB_PATH"]

@@ -17,7 +17,7 @@ SSM_F32 = 0
 SSM_BF16 = 1
 SSM_FLAG_ZOH = 1
 SSM_FLAG_REVERSE = 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_ALIGN",
            5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH", 8: "SSM_ERR_OVERLAP"}
@@ -35,8 +35,9 @@ class ssm_shape(ctypes.Structure):
 
 
 _lib = None
-EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update",
-           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_conv1d_fwd", "ssm_conv1d_update")
+EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_save",
+           "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_scan_bwd_saved_workspace_size",
+           "ssm_scan_bwd_saved", "ssm_conv1d_fwd", "ssm_conv1d_update")
 
 
 def load() -> ctypes.CDLL:
@@ -57,12 +58,18 @@ def load() -> ctypes.CDLL:
     lib.ssm_scan_workspace_size.restype = ctypes.c_size_t
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 11 + [vp, ctypes.c_size_t, vp]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_save.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 12 + [vp, ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd_save.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, u32] + [vp] * 10 + [vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ssm_shape)]
     lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ssm_scan_bwd.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 21 + [ctypes.c_size_t, vp]
     lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd_saved_workspace_size.argtypes = [ctypes.POINTER(ssm_shape)]
+    lib.ssm_scan_bwd_saved_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_bwd_saved.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 22 + [ctypes.c_size_t, vp]
+    lib.ssm_scan_bwd_saved.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 6 + [vp]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
     lib.ssm_conv1d_update.argtypes = [i64, i64, i64, i32] + [vp] * 5 + [vp]
@@ -136,15 +143,22 @@ def workspace_size(batch, dim, dstate, seqlen, io_dtype=SSM_BF16, zoh=False, rev
     return int(load().ssm_scan_workspace_size(ctypes.byref(sh)))
 
 
+def checkpoints_shape(batch, dim, dstate, seqlen):
+    """Shape of the block checkpoints scan_fwd(checkpoints=...) writes and scan_bwd reads."""
+    return (batch, (seqlen + 63) // 64, dim, dstate)
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *,
              out=None, final_state=True, zoh=False, reverse=False, workspace=None, split=True,
-             stream=None):
+             checkpoints=None, stream=None):
     """Selective scan.  u, delta, z: [B,D,L]; B, C: [B,N,L] (same dtype as u); A: [D,N] fp32;
     D, delta_bias: [D] fp32; initial_state: [B,D,N] fp32 or None.
     Returns (out [B,D,L] in u's dtype, final_state [B,D,N] fp32 or None).
     final_state may be True (allocate), False/None (not written) or a tensor to write into.
     workspace: a uint8 tensor of at least workspace_size(...) bytes, or None to allocate one;
-    split=False runs without a workspace (no sequence split)."""
+    split=False runs without a workspace (no sequence split).
+    checkpoints: an fp32 tensor of checkpoints_shape(...) to also write the state entering every
+    64-step block (ssm_scan_fwd_save), for scan_bwd(checkpoints=...)."""
     lib = load()
     Bsz, Dm, L = u.shape
     N = A.shape[1]
@@ -165,7 +179,8 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                              (delta_bias, (Dm,), f32, "delta_bias"),
                              (initial_state, (Bsz, Dm, N), f32, "initial_state"),
                              (out, (Bsz, Dm, L), u.dtype, "out"),
-                             (final_state, (Bsz, Dm, N), f32, "final_state")):
+                             (final_state, (Bsz, Dm, N), f32, "final_state"),
+                             (checkpoints, checkpoints_shape(Bsz, Dm, N, L), f32, "checkpoints")):
         _expect(t, shp, dt, name, device)
     ws_bytes = 0
     if workspace is not None and workspace.device != device:
@@ -178,9 +193,14 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
             ws_bytes = workspace.numel() * workspace.element_size()
     else:
         workspace = None
-    _check(lib.ssm_scan_fwd(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                            _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
-                            _ptr(workspace), ws_bytes, _stream(stream, device)))
+    if checkpoints is None:
+        _check(lib.ssm_scan_fwd(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                _ptr(workspace), ws_bytes, _stream(stream, device)))
+    else:
+        _check(lib.ssm_scan_fwd_save(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                     _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                     _ptr(checkpoints), _ptr(workspace), ws_bytes, _stream(stream, device)))
     return out, final_state
 
 
@@ -208,17 +228,22 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     return out
 
 
-def bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SSM_BF16, reverse=False) -> int:
+def bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SSM_BF16, reverse=False, saved=False) -> int:
+    """Workspace bytes of scan_bwd; saved=True: with the forward's checkpoints given."""
     sh = make_shape(batch, dim, dstate, seqlen, io_dtype, False, reverse)
-    return int(load().ssm_scan_bwd_workspace_size(ctypes.byref(sh)))
+    fn = load().ssm_scan_bwd_saved_workspace_size if saved else load().ssm_scan_bwd_workspace_size
+    return int(fn(ctypes.byref(sh)))
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *, dout,
-             dfinal_state=None, zoh=False, reverse=False, grads=None, workspace=None, stream=None):
+             dfinal_state=None, zoh=False, reverse=False, grads=None, workspace=None, checkpoints=None,
+             stream=None):
     """Gradients of scan_fwd for output gradient dout [B,D,L] (u's dtype) and optional
     final-state gradient [B,D,N] fp32.  Returns a dict: du, ddelta (u's dtype), dA [D,N], dB, dC
     [B,N,L], dD, ddelta_bias [D] (fp32), dz (u's dtype, None without z) and dinitial_state
-    [B,D,N] fp32.  grads: optional dict of preallocated outputs with those names."""
+    [B,D,N] fp32.  grads: optional dict of preallocated outputs with those names.
+    checkpoints: the tensor scan_fwd(checkpoints=...) wrote for the same inputs; the backward
+    then skips its own checkpoint pass (ssm_scan_bwd_saved)."""
     lib = load()
     Bsz, Dm, L = u.shape
     N = A.shape[1]
@@ -233,7 +258,8 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                              (delta_bias, (Dm,), f32, "delta_bias"),
                              (initial_state, (Bsz, Dm, N), f32, "initial_state"),
                              (dout, (Bsz, Dm, L), u.dtype, "dout"),
-                             (dfinal_state, (Bsz, Dm, N), f32, "dfinal_state")):
+                             (dfinal_state, (Bsz, Dm, N), f32, "dfinal_state"),
+                             (checkpoints, checkpoints_shape(Bsz, Dm, N, L), f32, "checkpoints")):
         _expect(t, shp, dt, name, device)
     shapes = dict(du=((Bsz, Dm, L), u.dtype), ddelta=((Bsz, Dm, L), u.dtype), dA=((Dm, N), f32),
                   dB=((Bsz, N, L), f32), dC=((Bsz, N, L), f32), dD=((Dm,), f32),
@@ -246,17 +272,22 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
         if g.get(k) is None:
             g[k] = torch.empty(shp, dtype=dt, device=dev)
         _expect(g[k], shp, dt, k, device)
-    need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(sh)))
+    size_fn = lib.ssm_scan_bwd_workspace_size if checkpoints is None else lib.ssm_scan_bwd_saved_workspace_size
+    need = int(size_fn(ctypes.byref(sh)))
     if workspace is not None and workspace.device != device:
         raise ValueError("workspace: expected a tensor on %s, got %s" % (device, workspace.device))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.ssm_scan_bwd(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                            _ptr(delta_bias), _ptr(initial_state), _ptr(dout), _ptr(dfinal_state),
-                            _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
-                            _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]),
-                            _ptr(workspace), ws_bytes, _stream(stream, device)))
+    outs = (_ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+            _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]))
+    ins = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+           _ptr(initial_state), _ptr(dout), _ptr(dfinal_state))
+    if checkpoints is None:
+        _check(lib.ssm_scan_bwd(ctypes.byref(sh), *ins, *outs, _ptr(workspace), ws_bytes, _stream(stream, device)))
+    else:
+        _check(lib.ssm_scan_bwd_saved(ctypes.byref(sh), *ins, _ptr(checkpoints), *outs, _ptr(workspace), ws_bytes,
+                                      _stream(stream, device)))
     return g
 
 

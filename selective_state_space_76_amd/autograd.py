@@ -1,4 +1,5 @@
-"""torch.autograd binding of the scan: forward through ssm_scan_fwd, backward through ssm_scan_bwd.
+"""torch.autograd binding of the scan: forward through ssm_scan_fwd_save (the outputs plus the block
+checkpoints), backward through ssm_scan_bwd_saved.
 
     from selective_state_space_76_amd import selective_scan
     out, last_state = selective_scan(u, delta, A, B, C, D, z, delta_bias)
@@ -14,24 +15,31 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import scan_bwd, scan_fwd
+from ._lib import checkpoints_shape, scan_bwd, scan_fwd
 
 
 class SelectiveScanFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, u, delta, A, B, C, D, z, delta_bias, initial_state, zoh, reverse):
-        out, final_state = scan_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, zoh=zoh, reverse=reverse)
-        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, initial_state)
+        # when a gradient will be asked for, the forward also writes the state entering every
+        # 64-step block, and the backward starts from them instead of recomputing them
+        ck = None
+        if any(ctx.needs_input_grad[:9]):
+            Bsz, Dm, L = u.shape
+            ck = torch.empty(checkpoints_shape(Bsz, Dm, A.shape[1], L), dtype=torch.float32, device=u.device)
+        out, final_state = scan_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, zoh=zoh, reverse=reverse,
+                                    checkpoints=ck)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, initial_state, ck)
         ctx.zoh, ctx.reverse = zoh, reverse
         return out, final_state
 
     @staticmethod
     def backward(ctx, dout, dfinal):
-        u, delta, A, B, C, D, z, delta_bias, initial_state = ctx.saved_tensors
+        u, delta, A, B, C, D, z, delta_bias, initial_state, ck = ctx.saved_tensors
         dout = torch.zeros_like(u) if dout is None else dout.to(u.dtype).contiguous()
         dfinal = None if dfinal is None else dfinal.float().contiguous()
         g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, initial_state, dout=dout, dfinal_state=dfinal,
-                     zoh=ctx.zoh, reverse=ctx.reverse)
+                     zoh=ctx.zoh, reverse=ctx.reverse, checkpoints=ck)
         need = ctx.needs_input_grad
 
         def cast(grad, like, i):

@@ -94,7 +94,7 @@ constexpr int kBwdTargetBlocks = 768;  // 3 backward workgroups per CU on 256 CU
 // into segments (whole 256-step chunks, >= 1024 steps) so that about kBwdTargetBlocks
 // workgroups run; each segment's checkpoints start from a carried state (summary pass + carry)
 // and its adjoint from a carried adjoint (adjoint summary + carry).
-bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl) {
+bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl, bool saved = false) {
   Plan fp;
   if (!make_plan(s, &fp)) return false;  // same size limits as the forward
   const int64_t Bsz = s->batch, Dm = s->dim, N = s->dstate, L = s->seqlen;
@@ -118,19 +118,21 @@ bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl) {
   const int64_t BD = Bsz * Dm, BDN = BD * N;
   int64_t x;
   if (!mul_ok(BDN, pl->nbk, &x)) return false;
-  pl->ckpt = round256(sizeof(float) * (size_t)x);
+  pl->ckpt = saved ? 0 : round256(sizeof(float) * (size_t)x);  // saved: the forward wrote them
   if (!mul_ok(2 * pl->nblk * Bsz * N, L, &x)) return false;
   pl->bc = round256(sizeof(float) * (size_t)x);
   if (!mul_ok(BDN, pl->S, &x)) return false;
   pl->a = round256(sizeof(float) * (size_t)x);
   pl->d = round256(sizeof(float) * (size_t)(2 * pl->S * BD));
   if (pl->S > 1) {
-    pl->seg_state = round256(sizeof(float) * (size_t)((pl->S - 1) * BDN));
-    pl->seg_dsum = round256(sizeof(float) * (size_t)((pl->S - 1) * BD));
-    pl->carries = round256(sizeof(float) * (size_t)(pl->S * BDN));
-    pl->adj_q = pl->carries;
+    if (!saved) {  // the checkpoints' own split: end states, step-size sums, carries
+      pl->seg_state = round256(sizeof(float) * (size_t)((pl->S - 1) * BDN));
+      pl->seg_dsum = round256(sizeof(float) * (size_t)((pl->S - 1) * BD));
+      pl->carries = round256(sizeof(float) * (size_t)(pl->S * BDN));
+    }
+    pl->adj_q = round256(sizeof(float) * (size_t)(pl->S * BDN));
     pl->adj_dsum = round256(sizeof(float) * (size_t)(pl->S * BD));
-    pl->adj_in = pl->carries;
+    pl->adj_in = pl->adj_q;
   }
   pl->total = pl->ckpt + pl->bc + pl->a + pl->d + pl->seg_state + pl->seg_dsum + pl->carries + pl->adj_q +
               pl->adj_dsum + pl->adj_in;
@@ -165,23 +167,30 @@ size_t ssm_scan_workspace_size(const ssm_shape* shape) {
   return pl.total;
 }
 
-ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta, const float* A,
-                        const void* B, const void* C, const float* D, const void* z,
-                        const float* delta_bias, const float* initial_state, void* out,
-                        float* final_state, void* workspace, size_t workspace_bytes,
-                        struct ihipStream_t* stream) {
+}  // extern "C"
+
+namespace {
+
+// ssm_scan_fwd, and with ckpt set ssm_scan_fwd_save (the state entering every 64-step block
+// is also written, [B, ceil(L/64), D, N] fp32).
+ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* z,
+                         const float* delta_bias, const float* initial_state, void* out,
+                         float* final_state, float* ckpt, void* workspace, size_t workspace_bytes,
+                         struct ihipStream_t* stream) {
   if (!shape) return SSM_ERR_NULL;
   if (shape->io_dtype != SSM_F32 && shape->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (shape->flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE)) return SSM_ERR_UNSUPPORTED;
   Plan pl;
   if (!make_plan(shape, &pl)) return SSM_ERR_SHAPE;
   if (!u || !delta || !A || !B || !C || !out) return SSM_ERR_NULL;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, workspace};
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, ckpt, workspace};
   for (const void* q : ptrs)
     if (misaligned(q)) return SSM_ERR_ALIGN;
 
   const int64_t Bsz = shape->batch, Dm = shape->dim, N = shape->dstate, L = shape->seqlen;
   const int64_t es = shape->io_dtype == SSM_BF16 ? 2 : 4;
+  const Range rc_ = span(ckpt, ckpt ? Bsz * Dm * N * ((L + 63) / 64) : 0, 4);
   const Range ins[] = {span(u, Bsz * Dm * L, es), span(delta, Bsz * Dm * L, es), span(A, Dm * N, 4),
                        span(B, Bsz * N * L, es), span(C, Bsz * N * L, es), span(D, D ? Dm : 0, 4),
                        span(z, z ? Bsz * Dm * L : 0, es), span(delta_bias, delta_bias ? Dm : 0, 4),
@@ -195,6 +204,9 @@ ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta
     if (!same_state && overlaps(rf, ins[i])) return SSM_ERR_OVERLAP;
   }
   if (overlaps(ro, rf)) return SSM_ERR_OVERLAP;
+  for (const Range& r : ins)
+    if (overlaps(rc_, r)) return SSM_ERR_OVERLAP;
+  if (overlaps(rc_, ro) || overlaps(rc_, rf)) return SSM_ERR_OVERLAP;
 
   const bool split = pl.S > 1 && workspace != nullptr;
   if (pl.S > 1 && workspace != nullptr && workspace_bytes < pl.total) return SSM_ERR_WORKSPACE;
@@ -203,13 +215,13 @@ ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta
     const Range rw = span(workspace, (int64_t)pl.total, 1);
     for (const Range& r : ins)
       if (overlaps(rw, r)) return SSM_ERR_OVERLAP;
-    if (overlaps(rw, ro) || overlaps(rw, rf)) return SSM_ERR_OVERLAP;
+    if (overlaps(rw, ro) || overlaps(rw, rf) || overlaps(rw, rc_)) return SSM_ERR_OVERLAP;
   }
 
   ssm::ScanParams p;
   memset(&p, 0, sizeof(p));
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias;
-  p.init = initial_state; p.out = out; p.final_state = final_state;
+  p.init = initial_state; p.out = out; p.final_state = final_state; p.ckpt = ckpt;
   p.Bsz = Bsz; p.Dm = Dm; p.N = N; p.L = L;
   p.nblk = (int)pl.nblk;
   p.vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;  // 16-byte chunks stay inside each row
@@ -235,6 +247,29 @@ ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta
   rc = launch_status(ssm::launch_carry(p, st));
   if (rc != SSM_OK) return rc;
   return launch_status(ssm::launch_scan(p, bf16, 0, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_scan_fwd(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, const float* initial_state, void* out,
+                        float* final_state, void* workspace, size_t workspace_bytes,
+                        struct ihipStream_t* stream) {
+  return scan_fwd_impl(shape, u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, nullptr,
+                       workspace, workspace_bytes, stream);
+}
+
+ssm_status ssm_scan_fwd_save(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, const float* initial_state, void* out,
+                             float* final_state, float* checkpoints, void* workspace,
+                             size_t workspace_bytes, struct ihipStream_t* stream) {
+  if (!checkpoints) return SSM_ERR_NULL;
+  return scan_fwd_impl(shape, u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, checkpoints,
+                       workspace, workspace_bytes, stream);
 }
 
 ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t io_dtype, uint32_t flags,
@@ -277,22 +312,34 @@ size_t ssm_scan_bwd_workspace_size(const ssm_shape* shape) {
   return pl.total;
 }
 
-ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta, const float* A,
-                        const void* B, const void* C, const float* D, const void* z,
-                        const float* delta_bias, const float* initial_state, const void* dout,
-                        const float* dfinal_state, void* du, void* ddelta, float* dA, float* dB,
-                        float* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
-                        void* workspace, size_t workspace_bytes, struct ihipStream_t* stream) {
+size_t ssm_scan_bwd_saved_workspace_size(const ssm_shape* shape) {
+  BwdPlan pl;
+  if (!make_bwd_plan(shape, &pl, true)) return 0;
+  return pl.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// ssm_scan_bwd, and with saved set ssm_scan_bwd_saved (the checkpoints come from
+// ssm_scan_fwd_save instead of a checkpoint pass).
+ssm_status scan_bwd_impl(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* z,
+                         const float* delta_bias, const float* initial_state, const void* dout,
+                         const float* dfinal_state, const float* saved, void* du, void* ddelta, float* dA,
+                         float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
+                         void* workspace, size_t workspace_bytes, struct ihipStream_t* stream) {
   if (!shape) return SSM_ERR_NULL;
   if (shape->io_dtype != SSM_F32 && shape->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (shape->flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE)) return SSM_ERR_UNSUPPORTED;
   BwdPlan pl;
-  if (!make_bwd_plan(shape, &pl)) return SSM_ERR_SHAPE;
+  if (!make_bwd_plan(shape, &pl, saved != nullptr)) return SSM_ERR_SHAPE;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC || !workspace)
     return SSM_ERR_NULL;
   if (z && !dz) return SSM_ERR_NULL;
   if (!z) dz = nullptr;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, initial_state, dout, dfinal_state, du,
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, initial_state, dout, dfinal_state, saved, du,
                         ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace};
   for (const void* q : ptrs)
     if (misaligned(q)) return SSM_ERR_ALIGN;
@@ -305,7 +352,8 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
                        span(C, BNL, es), span(D, D ? Dm : 0, 4), span(z, z ? BDL : 0, es),
                        span(delta_bias, delta_bias ? Dm : 0, 4),
                        span(initial_state, initial_state ? BDN : 0, 4), span(dout, BDL, es),
-                       span(dfinal_state, dfinal_state ? BDN : 0, 4)};
+                       span(dfinal_state, dfinal_state ? BDN : 0, 4),
+                       span(saved, saved ? BDN * pl.nbk : 0, 4)};
   const Range outs[] = {span(du, BDL, es), span(ddelta, BDL, es), span(dA, Dm * N, 4), span(dB, BNL, 4),
                         span(dC, BNL, 4), span(dD, dD ? Dm : 0, 4), span(dz, dz ? BDL : 0, es),
                         span(ddelta_bias, ddelta_bias ? Dm : 0, 4),
@@ -324,7 +372,7 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   char* ws = static_cast<char*>(workspace);
   size_t off = 0;
   auto take = [&](size_t bytes) { float* q = reinterpret_cast<float*>(ws + off); off += bytes; return q; };
-  float* ckpt = take(pl.ckpt);
+  float* ckpt = saved ? const_cast<float*>(saved) : take(pl.ckpt);  // read only when saved
   float* part_bc = take(pl.bc);
   float* part_a = take(pl.a);
   float* part_d = take(pl.d);
@@ -341,30 +389,32 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   const int64_t SB = pl.S * Bsz;
 
   // checkpoints: the state entering every 64-step block (a split sequence: each segment from
-  // its carry, as in the forward's split)
-  ssm::ScanParams fp;
-  memset(&fp, 0, sizeof(fp));
-  fp.u = u; fp.delta = delta; fp.A = A; fp.B = B; fp.C = C; fp.bias = delta_bias; fp.init = initial_state;
-  fp.ckpt = ckpt;
-  fp.Bsz = Bsz; fp.Dm = Dm; fp.N = N; fp.L = L;
-  fp.S = (int)pl.S;
-  fp.seg_len = split ? pl.seg_len : pl.nbk * 64;
-  fp.nblk = (int)pl.nblk;
-  fp.vec = vec;
-  fp.reverse = rev;
-  fp.zoh = zoh;
-  ssm_status rc;
-  if (split) {
-    fp.seg_state = seg_state;
-    fp.seg_dsum = seg_dsum;
-    rc = launch_status(ssm::launch_scan(fp, bf16, 1, st));
-    if (rc != SSM_OK) return rc;
-    fp.carries = carries;
-    rc = launch_status(ssm::launch_carry(fp, st));
+  // its carry, as in the forward's split), unless the forward saved them
+  ssm_status rc = SSM_OK;
+  if (!saved) {
+    ssm::ScanParams fp;
+    memset(&fp, 0, sizeof(fp));
+    fp.u = u; fp.delta = delta; fp.A = A; fp.B = B; fp.C = C; fp.bias = delta_bias; fp.init = initial_state;
+    fp.ckpt = ckpt;
+    fp.Bsz = Bsz; fp.Dm = Dm; fp.N = N; fp.L = L;
+    fp.S = (int)pl.S;
+    fp.seg_len = split ? pl.seg_len : pl.nbk * 64;
+    fp.nblk = (int)pl.nblk;
+    fp.vec = vec;
+    fp.reverse = rev;
+    fp.zoh = zoh;
+    if (split) {
+      fp.seg_state = seg_state;
+      fp.seg_dsum = seg_dsum;
+      rc = launch_status(ssm::launch_scan(fp, bf16, 1, st));
+      if (rc != SSM_OK) return rc;
+      fp.carries = carries;
+      rc = launch_status(ssm::launch_carry(fp, st));
+      if (rc != SSM_OK) return rc;
+    }
+    rc = launch_status(ssm::launch_ckpt(fp, bf16, st));
     if (rc != SSM_OK) return rc;
   }
-  rc = launch_status(ssm::launch_ckpt(fp, bf16, st));
-  if (rc != SSM_OK) return rc;
 
   ssm::BwdParams bp;
   memset(&bp, 0, sizeof(bp));
@@ -403,6 +453,34 @@ ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta
   }
   if (ddelta_bias) rc = launch_status(ssm::launch_reduce(ddelta_bias, part_d + SB * Dm, SB, Dm, Dm, st));
   return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_scan_bwd(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, const float* initial_state, const void* dout,
+                        const float* dfinal_state, void* du, void* ddelta, float* dA, float* dB,
+                        float* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
+                        void* workspace, size_t workspace_bytes, struct ihipStream_t* stream) {
+  return scan_bwd_impl(shape, u, delta, A, B, C, D, z, delta_bias, initial_state, dout, dfinal_state, nullptr,
+                       du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace, workspace_bytes,
+                       stream);
+}
+
+ssm_status ssm_scan_bwd_saved(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                              const void* B, const void* C, const float* D, const void* z,
+                              const float* delta_bias, const float* initial_state, const void* dout,
+                              const float* dfinal_state, const float* checkpoints, void* du, void* ddelta,
+                              float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                              float* dinitial_state, void* workspace, size_t workspace_bytes,
+                              struct ihipStream_t* stream) {
+  if (!checkpoints) return SSM_ERR_NULL;
+  return scan_bwd_impl(shape, u, delta, A, B, C, D, z, delta_bias, initial_state, dout, dfinal_state,
+                       checkpoints, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, workspace,
+                       workspace_bytes, stream);
 }
 
 ssm_status ssm_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int32_t io_dtype,

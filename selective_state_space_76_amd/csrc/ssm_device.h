@@ -178,7 +178,8 @@ __device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
   return out;
 }
 
-// MODE 0: output pass (writes out and, for the last segment, final_state).
+// MODE 0: output pass (writes out and, for the last segment, final_state; with
+//         ckpt set also the state entering every 64-step block, for the backward).
 // MODE 1: summary pass over segments 0..S-2 (writes seg_state and seg_dsum).
 // MODE 2: checkpoint pass for the backward (writes the state entering every
 //         64-step block to ckpt; a split sequence starts each segment from its carry).
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
       if (t0 + 64 < te) fetch(t0 + 64);  // next block streams in while this one is computed
       __syncthreads();  // tile visible
     }
-    if (MODE == 2 && dval) {
+    if ((MODE == 2 || (MODE == 0 && p.ckpt != nullptr)) && dval) {  // the state entering the block
       const int64_t nbk = (L + 63) / 64;
 #pragma unroll
       for (int i = 0; i < NL; ++i)

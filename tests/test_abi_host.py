@@ -230,3 +230,53 @@ def test_bwd_errors():
     assert bwd(shp(), dC=fake(10, off=256)) == 8            # two outputs overlap
     assert bwd(shp(), ws=fake(9)) == 8                      # workspace over an output
     assert bwd(shp(flags=L.SSM_FLAG_REVERSE), du=fake(1, off=64)) == 8
+
+
+def scan_save(shape, ck, ws=None, ws_bytes=0, **kw):
+    lib = L.load()
+    p = good_ptrs()
+    p.update(kw)
+    args = [p.get(n) for n in ("u", "delta", "A", "B", "C", "D", "z", "bias", "h0", "out", "fs")]
+    return lib.ssm_scan_fwd_save(None if shape is None else ctypes.byref(shape), *args, ck, ws, ws_bytes, None)
+
+
+def bwd_saved(shape, ck, ws_bytes=None, **kw):
+    lib = L.load()
+    names = ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0", "dout", "dfin"]
+    onames = ["du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "ws"]
+    p = dict(u=fake(1), delta=fake(2), A=fake(3), B=fake(4), C=fake(5), dout=fake(6), du=fake(7), ddelta=fake(8),
+             dA=fake(9), dB=fake(10), dC=fake(11), ws=fake(12))
+    p.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.ssm_scan_bwd_saved_workspace_size(ctypes.byref(shape)) if shape is not None else 0
+    return lib.ssm_scan_bwd_saved(None if shape is None else ctypes.byref(shape), *[p.get(n) for n in names], ck,
+                                  *[p.get(n) for n in onames], ws_bytes, None)
+
+
+def test_saved_checkpoint_entry_points():
+    # the forward that saves checkpoints and the backward that reads them: the checks of the
+    # plain entry points, plus the checkpoint buffer's own (required, aligned, no overlap)
+    lib = L.load()
+    s = shp()                                        # 2 x 64 x 16 x 128: checkpoints 2 x 2 x 64 x 16 fp32
+    ck_bytes = 4 * 2 * 2 * 64 * 16
+    assert scan_save(s, None) == 1
+    assert scan_save(None, fake(13)) == 1
+    assert scan_save(s, fake(13, off=4)) == 4
+    assert scan_save(s, fake(1, off=64)) == 8        # inside u
+    assert scan_save(s, fake(13), out=fake(13, off=ck_bytes - 16)) == 8
+    assert scan_save(s, fake(13), fs=fake(13, off=256)) == 8
+    assert scan_save(shp(dstate=65), fake(13)) == 2
+    assert scan_save(s, fake(13), u=None) == 1
+    assert bwd_saved(s, None) == 1
+    assert bwd_saved(s, fake(13, off=4)) == 4
+    assert bwd_saved(s, fake(13), du=fake(13, off=ck_bytes - 16)) == 8  # an output inside the checkpoints
+    assert bwd_saved(s, fake(13), ws=fake(13, off=64)) == 8
+    assert bwd_saved(s, fake(13), ws_bytes=lib.ssm_scan_bwd_saved_workspace_size(ctypes.byref(s)) - 1) == 6
+    # the saved backward's workspace is the plain one without the checkpoints (and their split)
+    r = lambda x: (x + 255) // 256 * 256
+    assert (lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) - lib.ssm_scan_bwd_saved_workspace_size(ctypes.byref(s))
+            == r(ck_bytes))
+    s = shp(batch=1, dim=20, dstate=16, seqlen=5000)  # split: 5 segments
+    S, bdn, bd = 5, 320, 20
+    assert (lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) - lib.ssm_scan_bwd_saved_workspace_size(ctypes.byref(s))
+            == r(4 * bdn * ((5000 + 63) // 64)) + r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn))

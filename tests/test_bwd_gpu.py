@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from selective_state_space_76_amd import SSM_F32, bwd_workspace_size, scan_bwd
+from selective_state_space_76_amd import SSM_F32, bwd_workspace_size, checkpoints_shape, scan_bwd, scan_fwd
 from selective_state_space_76_amd import workloads as W
 from tests.gpu_util import rel_err, tol_for
 
@@ -223,3 +223,47 @@ def test_bwd_dB_dC_add_over_channel_halves():
         e = rel_err(full[k], s.double().cpu().numpy())
         print("halves %s rel_err %.2g" % (k, e), flush=True)
         assert e <= 1e-5, (k, e)
+
+
+# The forward that saves its block checkpoints (ssm_scan_fwd_save) and the backward that starts
+# from them (ssm_scan_bwd_saved): the forward's outputs are unchanged, each checkpoint is the
+# oracle's state after the first 64 k steps, and the gradients match the oracle.
+@pytest.mark.parametrize("Bsz,Dm,N,L,zoh,reverse", [
+    (2, 24, 16, 300, False, False), (2, 24, 64, 300, True, True), (2, 20, 16, 7, False, True),
+    (1, 20, 16, 5000, False, False), (1, 20, 40, 5000, True, True), (1, 24, 64, 4100, False, True)],
+    ids=["16", "64zr", "short", "split16", "split40zr", "split64r"])
+def test_saved_checkpoints(Bsz, Dm, N, L, zoh, reverse):
+    print("case: saved checkpoints %dx%dx%dx%d zoh=%d reverse=%d f32" % (Bsz, Dm, N, L, zoh, reverse), flush=True)
+    x = make(Bsz, Dm, N, L, torch.float32, seed=11 * N + L, h0=True, dfin=True)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    args = (d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], d["h0"])
+    ck = torch.full(checkpoints_shape(Bsz, Dm, N, L), float("nan"), device=DEV)
+    out1, fs1 = scan_fwd(*args, zoh=zoh, reverse=reverse, checkpoints=ck)
+    out0, fs0 = scan_fwd(*args, zoh=zoh, reverse=reverse)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out0) and torch.equal(fs1, fs0)
+    ckh = ck.cpu()
+    nbk = ckh.shape[1]
+    tol = tol_for(x["u"])
+    for k in sorted({0, min(1, nbk - 1), nbk // 2, nbk - 1}):
+        if k == 0:
+            ref = x["h0"].double().numpy()
+        else:
+            t = 64 * k  # the logical prefix of t steps (for a reverse scan, the last t physical steps)
+            sl = (lambda v: v[..., L - t:]) if reverse else (lambda v: v[..., :t])
+            _, ref = oracle.scan(sl(x["u"]), sl(x["delta"]), x["A"], sl(x["B"]), sl(x["C"]), D=x["D"],
+                                 delta_bias=x["delta_bias"], h0=x["h0"], zoh=zoh, reverse=reverse)
+        e = rel_err(ckh[:, k], ref)
+        print("checkpoint %d rel_err %.3g" % (k, e), flush=True)
+        assert e <= tol, (k, e)
+    g_saved = scan_bwd(*args, dout=d["dout"], dfinal_state=d["dfin"], zoh=zoh, reverse=reverse, checkpoints=ck)
+    g_plain = run(x, reverse, zoh)
+    ref = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], x["h0"],
+                          dout=x["dout"], dfinal=x["dfin"], zoh=zoh, reverse=reverse)
+    errs = {k: rel_err(g_saved[k], ref[ORACLE_NAME.get(k, k)]) for k in NAMES
+            if g_saved[k] is not None and ref[ORACLE_NAME.get(k, k)] is not None}
+    same = all(torch.equal(g_saved[k], g_plain[k]) for k in NAMES if g_saved[k] is not None)
+    print("rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()) + "; bitwise equal to the plain backward: %s"
+          % same, flush=True)
+    bad = {k: e for k, e in errs.items() if not e <= tol}
+    assert not bad, bad
