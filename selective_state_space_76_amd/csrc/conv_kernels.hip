@@ -77,7 +77,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Vector path.  A wave owns 64*P consecutive chunks (P passes of 64 lanes); all P loads are
 // issued before any arithmetic so each lane keeps P * 16 bytes in flight.  The inputs before
 // lane l's chunk are the tail of lane l-1's chunk in the same pass; lane 0 takes lane 63's
-// tail from the previous pass, or (first pass) reads it from memory.
+// tail from the previous pass, or (first pass) the tail of the chunk before the wave's first,
+// loaded with the others (so no wave waits on a second round trip to memory; 25.1 -> 24.0 us
+// per call at 8 x 1536 x 2048).
 template <typename IO, int K, int P, bool NT = true>
 __global__ __launch_bounds__(256) void conv_vec_kernel(ConvParams p) {
   constexpr int V = 16 / (int)sizeof(IO);
@@ -91,21 +93,21 @@ __global__ __launch_bounds__(256) void conv_vec_kernel(ConvParams p) {
   const IO* x = static_cast<const IO*>(p.x);
   IO* u = static_cast<IO*>(p.u);
 
+  // every load is issued before any arithmetic: the P chunks, lane 0's previous chunk (its tail
+  // is the halo of the wave's first chunk) and, at row starts, the carried state
   u32x4 q[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int64_t gid = wbase + 64 * j + lane;
-    q[j] = u32x4{0u, 0u, 0u, 0u};
-    if (gid < total) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(x + gid * V);
-      q[j] = NT ? __builtin_nontemporal_load(src) : *src;
-    }
-  }
-
+  int64_t rows[P], cs[P];
+  float sv[P][H > 0 ? H : 1];
+  const IO* st = static_cast<const IO*>(p.state_in);
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int64_t gid = wbase + 64 * j + lane;
     const bool valid = gid < total;
+    q[j] = u32x4{0u, 0u, 0u, 0u};
+    if (valid) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + gid * V);
+      q[j] = NT ? __builtin_nontemporal_load(src) : *src;
+    }
     int64_t row, c;
     if (total <= 0xffffffffll) {  // uniform: 32-bit division when the chunk count allows
       const uint32_t g32 = (uint32_t)(valid ? gid : 0), c32 = (uint32_t)cpr;
@@ -115,6 +117,27 @@ __global__ __launch_bounds__(256) void conv_vec_kernel(ConvParams p) {
       row = valid ? gid / cpr : 0;
       c = valid ? gid - row * cpr : 0;
     }
+    rows[j] = row;
+    cs[j] = c;
+#pragma unroll
+    for (int k = 0; k < (H > 0 ? H : 1); ++k) sv[j][k] = 0.0f;
+    if constexpr (H > 0) {
+      if (valid && c == 0 && st) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) sv[j][k] = ld(st, row * H + k);
+      }
+    }
+  }
+  u32x4 qp = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (H > 0) {
+    if (lane == 0 && wbase > 0 && wbase < total) qp = *reinterpret_cast<const u32x4*>(x + (wbase - 1) * V);
+  }
+
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int64_t gid = wbase + 64 * j + lane;
+    const bool valid = gid < total;
+    const int64_t row = rows[j], c = cs[j];
     float xs[V];
     unpack(uint4{q[j].x, q[j].y, q[j].z, q[j].w}, xs);
 
@@ -129,20 +152,15 @@ __global__ __launch_bounds__(256) void conv_vec_kernel(ConvParams p) {
           const uint32_t pw[4] = {q[j - 1].x, q[j - 1].y, q[j - 1].z, q[j - 1].w};
           const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)pw[i], 63);
           if (lane == 0) tw[i] = last;
+        } else {
+          const uint32_t pq[4] = {qp.x, qp.y, qp.z, qp.w};
+          if (lane == 0) tw[i] = pq[i];
         }
       }
       float prev[V];
       unpack(uint4{tw[0], tw[1], tw[2], tw[3]}, prev);
 #pragma unroll
-      for (int k = 0; k < H; ++k) hal[k] = prev[V - H + k];
-      if (c == 0) {
-        const IO* st = static_cast<const IO*>(p.state_in);
-#pragma unroll
-        for (int k = 0; k < H; ++k) hal[k] = st ? ld(st, row * H + k) : 0.0f;
-      } else if (j == 0 && lane == 0 && valid) {
-#pragma unroll
-        for (int k = 0; k < H; ++k) hal[k] = ld(x, gid * V - H + k);
-      }
+      for (int k = 0; k < H; ++k) hal[k] = c == 0 ? sv[j][k] : prev[V - H + k];
     }
     if (!valid) continue;
 
