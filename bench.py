@@ -8,8 +8,9 @@ scan, carry, output epilogue: the entire prefill/training-forward path) with
 every input already resident in HBM.  The timed loop rotates through enough
 independent input sets that they cannot be served from the 256 MB Infinity
 Cache.  The same JSON line also carries the decode path (ssm_state_update) on
-the 2.8B-shaped generation workload, the backward pass (ssm_scan_bwd) on the
-same workload, the conv + SiLU step that produces u
+the 2.8B-shaped generation workload, the backward pass (ssm_scan_bwd; as context
+also its ZOH variant and ssm_scan_bwd_saved from a saving forward's checkpoints) on
+the same workload, the conv + SiLU step that produces u
 (ssm_conv1d_fwd on the same [B, D, L] shape, ssm_conv1d_update on the decode
 shape) and the fp64 CPU oracle's rate on the host.
 
