@@ -17,9 +17,10 @@ DEV = "cuda"
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
 @pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
-def test_autograd_matches_oracle(dtype, reverse, zoh):
+def test_autograd_matches_oracle(dtype, reverse, zoh, shape=(2, 40, 16, 300)):
     name = "tiny" if dtype == torch.float32 else "mamba130m"
-    w = W.WORKLOADS[name].with_shape(batch=2, dim=40, dstate=16, seqlen=300, seed=8000 + reverse + 2 * zoh)
+    Bsz, Dm, N, L = shape
+    w = W.WORKLOADS[name].with_shape(batch=Bsz, dim=Dm, dstate=N, seqlen=L, seed=8000 + reverse + 2 * zoh)
     x = W.scan_inputs(w)
     gen = torch.Generator().manual_seed(8100)
     h0 = torch.randn(w.batch, w.dim, w.dstate, generator=gen)
@@ -43,6 +44,13 @@ def test_autograd_matches_oracle(dtype, reverse, zoh):
         assert v.grad.dtype == v.dtype, k
     bad = {k: e for k, e in errs.items() if not e <= tol_for(x["u"])}
     assert not bad, bad
+
+
+# a shape with few channels and a long sequence: the forward and the backward both split the
+# sequence, and the backward starts from the checkpoints the forward saved
+@pytest.mark.parametrize("reverse,zoh", [(False, False), (True, True)], ids=["fwd-euler", "rev-zoh"])
+def test_autograd_split_sequence(reverse, zoh):
+    test_autograd_matches_oracle(torch.float32, reverse, zoh, shape=(1, 24, 32, 4200))
 
 
 def test_autograd_only_final_state_used():
