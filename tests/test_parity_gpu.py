@@ -217,3 +217,31 @@ def test_state_update_zoh(dtype):
                                    zoh=True)
         tol = 1e-4 if dtype == torch.float32 else 2e-2
         assert rel_err(y, ref_y) <= tol and rel_err(st, state) <= tol
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("N", [16, 64])
+def test_zero_and_tiny_decay(zoh, N):
+    """Some A entries exactly 0 (no decay: the state sums its inputs; under ZOH the factor's
+    1/A is infinite and the series takes over) and others tiny, in the scan (whole and split
+    sequence) and in the decode step."""
+    print("case: A = 0 and A = -1e-4 entries, zoh=%d N=%d" % (zoh, N), flush=True)
+    for L in (300, 4200):
+        x = make(1, 24, N, L, dtype=torch.float32, seed=900 + N + L)
+        A = x["A"].clone()
+        A[::3, ::2] = 0.0
+        A[1::3, 1::4] = -1e-4
+        x["A"] = A
+        full_check(x, zoh=zoh)
+    w = W.WORKLOADS["decode2p8b"].with_shape(batch=3, dim=24, dstate=N, seed=950 + N)
+    A = torch.full((24, N), -0.5)
+    A[::3, ::2] = 0.0
+    A[1::3, 1::4] = -1e-4
+    s = W.decode_inputs(w, 0)
+    st0 = torch.randn(3, 24, N, generator=torch.Generator().manual_seed(951))
+    st = st0.to(DEV)
+    y = state_update(st, s["u"].float().to(DEV), s["delta"].float().to(DEV), A.to(DEV), s["B"].float().to(DEV),
+                     s["C"].float().to(DEV), zoh=zoh)
+    torch.cuda.synchronize()
+    ry, rst = oracle.step(st0.double(), s["u"].float(), s["delta"].float(), A, s["B"].float(), s["C"].float(), zoh=zoh)
+    assert rel_err(y, ry) <= 1e-4 and rel_err(st, rst) <= 1e-4
