@@ -58,17 +58,16 @@ __device__ __forceinline__ void store_io(bf16_t* p, float v) {
   *p = __builtin_bit_cast(bf16_t, (__bf16)v);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
-// log(1 + e^x).  Above 20 the answer is x to within 2e-9 relative.  Below, with
-// e = e^x and w = fl(1 + e), log1p(e) = log(w) + log(1 + d/w) where d = e - (w - 1)
-// is the exact rounding error of w (Sterbenz); |d/w| <= 2^-24, so adding d
-// instead of log(1 + d/w) errs by under 2^-25 absolute, while it restores the
-// bits of e that w lost when e is small.
+// log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  With e = e^-|x| <= 1 and w = fl(1 + e) in
+// [1, 2], log1p(e) = log(w) + log(1 + d/w) where d = e - (w - 1) is the exact rounding
+// error of w (Sterbenz); adding d instead of log(1 + d/w) errs by under |d| (1 - 1/w) <=
+// 2^-25 absolute, while it restores the bits of e that w lost when e is small.  (With
+// e^x itself, w grows without bound and so does that error: 0.5 at x = 16.)
 __device__ __forceinline__ float softplus_(float x) {
-  const float e = exp2_(x * kLog2e);
+  const float e = exp2_(-fabsf(x) * kLog2e);
   const float w = 1.0f + e;
   const float d = e - (w - 1.0f);
-  const float r = __builtin_fmaf(log2_(w), kLn2, d);
-  return x > 20.0f ? x : r;
+  return fmaxf(x, 0.0f) + __builtin_fmaf(log2_(w), kLn2, d);
 }
 
 __device__ __forceinline__ float silu_(float z) { return z * rcp_(1.0f + exp2_(-z * kLog2e)); }

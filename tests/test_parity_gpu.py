@@ -245,3 +245,25 @@ def test_zero_and_tiny_decay(zoh, N):
     torch.cuda.synchronize()
     ry, rst = oracle.step(st0.double(), s["u"].float(), s["delta"].float(), A, s["B"].float(), s["C"].float(), zoh=zoh)
     assert rel_err(y, ry) <= 1e-4 and rel_err(st, rst) <= 1e-4
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+def test_wide_step_sizes(zoh):
+    """delta + bias spread over [-30, 30]: softplus from its exponential tail to the linear
+    branch above 20 (dt = x there), decays from ~1 to exactly 0 in fp32, in the scan and the
+    backward."""
+    print("case: wide step sizes, zoh=%d" % zoh, flush=True)
+    x = make(2, 20, 16, 400, dtype=torch.float32, seed=990 + zoh)
+    g = torch.Generator().manual_seed(991)
+    x["delta"] = (torch.rand(x["delta"].shape, generator=g) * 60.0 - 30.0).float()
+    x["delta_bias"] = torch.zeros_like(x["delta_bias"])
+    full_check(x, zoh=zoh)
+    from selective_state_space_76_amd import scan_bwd
+    d = dev(x)
+    gr = scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], dout=d["u"], zoh=zoh)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], None,
+                          dout=x["u"], dfinal=None, zoh=zoh)
+    errs = {k: rel_err(gr[k], ref[k]) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias")}
+    print("rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()), flush=True)
+    assert all(e <= 1e-4 for e in errs.values()), errs
