@@ -64,6 +64,25 @@ static double softplus_f64(double x) {
 
 static double silu_f64(double z) { return z / (1.0 + exp(-z)); }
 
+/* Zero-order hold (freeguideonline tutorial, section 2.2): B_bar = e B with
+   e = (exp(dt A) - 1) / A, taken as expm1(dt A) / A so that it keeps its digits as dt A -> 0.
+   Its derivative in A, de/dA = (dt exp(dt A) - e) / A, cancels there; for |dt A| < 1e-2 it is
+   taken from its Taylor series dt^2 sum_k (k + 1) (dt A)^k / (k + 2)!, whose terms past k = 6
+   are below the fp64 rounding level (at A = 0 the series is the limit dt^2 / 2). */
+static double zoh_e_dA_f64(double dt, double an, double a, double e) {
+  const double x = dt * an;
+  if (fabs(x) < 1e-2) {
+    double s = 0.0, f = 2.0, p = 1.0; /* f = (k + 2)!, p = x^k */
+    for (int k = 0; k <= 6; ++k) {
+      s += (k + 1) * p / f;
+      p *= x;
+      f *= (k + 3);
+    }
+    return dt * dt * s;
+  }
+  return (dt * a - e) / an;
+}
+
 int oracle_abi_version(void) { return 5; }
 
 /* Threads an OpenMP region of the oracle uses by default (1 without OpenMP). */
@@ -112,7 +131,7 @@ int oracle_scan_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
         const double abar = exp(dt * a_dn);
         double bbar;
         if ((flags & ORACLE_ZOH) && a_dn != 0.0)
-          bbar = (abar - 1.0) / a_dn * Ab[n * L + t];
+          bbar = expm1(dt * a_dn) / a_dn * Ab[n * L + t];
         else
           bbar = dt * Ab[n * L + t];
         h[n] = abar * h[n] + bbar * ur[t];
@@ -151,7 +170,7 @@ int oracle_step_f64(int64_t Bsz, int64_t Dm, int64_t N, double* state,
       const double abar = exp(dt * a_dn);
       double bbar;
       if ((flags & ORACLE_ZOH) && a_dn != 0.0)
-        bbar = (abar - 1.0) / a_dn * Bm[b * N + n];
+        bbar = expm1(dt * a_dn) / a_dn * Bm[b * N + n];
       else
         bbar = dt * Bm[b * N + n];
       double* h = state + r * N + n;
@@ -280,7 +299,7 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
           for (int64_t n = 0; n < N; ++n) {
             const double an = A[d * N + n];
             const double a = exp(dt * an);
-            const double e = (zoh && an != 0.0) ? (a - 1.0) / an : dt;
+            const double e = (zoh && an != 0.0) ? expm1(dt * an) / an : dt;
             const double h = a * hs[s * N + n] + e * Ab[n * L + t] * ur[t];
             hs[(s + 1) * N + n] = h;
             acc += Cb[n * L + t] * h;
@@ -307,9 +326,9 @@ int oracle_scan_bwd_f64(int64_t Bsz, int64_t Dm, int64_t N, int64_t L,
             const double an = A[d * N + n];
             const double a = exp(dt * an);
             const double hp = hs[s * N + n];
-            const double e = (zoh && an != 0.0) ? (a - 1.0) / an : dt;  /* B_bar / B */
+            const double e = (zoh && an != 0.0) ? expm1(dt * an) / an : dt;  /* B_bar / B */
             const double e_dt = zoh ? a : 1.0;                             /* de/ddt */
-            const double e_dA = !zoh ? 0.0 : (an != 0.0 ? (dt * a - e) / an : 0.5 * dt * dt);
+            const double e_dA = !zoh ? 0.0 : zoh_e_dA_f64(dt, an, a, e);
             G[n] += dy * Cb[n * L + t];
             sC[n * L + t] += dy * hs[(s + 1) * N + n];
             dut += G[n] * e * Ab[n * L + t];

@@ -513,6 +513,33 @@ def check_bwd_zoh_at_zero_decay(orc):
     assert abs((yp - ym)[0, 0, 0] / (2 * eps) - want) < 1e-7
 
 
+def check_zoh_near_zero_decay_exact(orc):
+    """ZOH close to A = 0, against its closed forms evaluated in 60-digit decimal arithmetic
+    (where exp(dt A) - 1 and dt exp(dt A) - e lose nothing to cancellation).  One step from a
+    zero state with no skip and no gate: out_0 = C e B u with e = (exp(dt A) - 1) / A, and
+    d out_0 / dA = C B u (dt exp(dt A) - e) / A.  In fp64 the plain closed forms lose up to
+    ~1e-16 / (dt A)^2 relative here; the oracle must not."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    x = np.array([[[0.4]]])
+    u = np.array([[[1.3]]])
+    Bm = np.array([[[0.6]]])
+    Cm = np.array([[[-1.7]]])
+    dt = float(np.logaddexp(0.0, 0.4))
+    cbu = Decimal(Cm[0, 0, 0]) * Decimal(Bm[0, 0, 0]) * Decimal(u[0, 0, 0])
+    for a in (-1e-6, 3e-7, -2e-3, 2e-2, -0.05, -1.0):
+        A = np.array([[a]])
+        y, _ = orc.scan(u, x, A, Bm, Cm, zoh=True)
+        g = orc.scan_bwd(u, x, A, Bm, Cm, dout=np.array([[[1.0]]]), zoh=True)
+        D_dt, D_A = Decimal(dt), Decimal(a)
+        ex = (D_dt * D_A).exp()
+        e = (ex - 1) / D_A
+        want_y = float(cbu * e)
+        want_dA = float(cbu * (D_dt * ex - e) / D_A)
+        assert abs(y[0, 0, 0] - want_y) <= 1e-14 * abs(want_y), (a, y[0, 0, 0], want_y)
+        assert abs(g["dA"][0, 0] - want_dA) <= 1e-13 * abs(want_dA), (a, g["dA"][0, 0], want_dA)
+
+
 ALL_CHECKS = [check_brute_force, check_initial_state, check_lti_closed_form, check_zoh_library,
               check_a_zero_cumsum, check_small_step_skip, check_single_step_closed_form,
               check_step_matches_scan, check_softplus_silu, check_linearity_in_u, check_causality,
@@ -520,4 +547,4 @@ ALL_CHECKS = [check_brute_force, check_initial_state, check_lti_closed_form, che
               check_conv_library, check_conv_impulse, check_conv_k1, check_conv_state_out,
               check_conv_chunking, check_conv_causality,
               check_bwd_autograd, check_bwd_finite_difference, check_bwd_scalar_closed_form,
-              check_bwd_zoh_at_zero_decay]
+              check_bwd_zoh_at_zero_decay, check_zoh_near_zero_decay_exact]

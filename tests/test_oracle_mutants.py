@@ -13,8 +13,8 @@ MUTANTS = [
     ("y_from_old_state",
      "h[n] = abar * h[n] + bbar * ur[t];\n        acc += Cb[n * L + t] * h[n];",
      "acc += Cb[n * L + t] * h[n];\n        h[n] = abar * h[n] + bbar * ur[t];"),
-    ("sign_of_A", "const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab",
-     "const double abar = exp(-dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab"),
+    ("sign_of_A", "const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = expm1(dt * a_dn) / a_dn * Ab",
+     "const double abar = exp(-dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = expm1(dt * a_dn) / a_dn * Ab"),
     ("bias_outside_softplus", "softplus_f64(dr[t] + (bias ? bias[d] : 0.0))",
      "(softplus_f64(dr[t]) + (bias ? bias[d] : 0.0))"),
     ("B_transposed", "bbar = dt * Ab[n * L + t];", "bbar = dt * Ab[t * N + n];"),
@@ -30,10 +30,10 @@ MUTANTS = [
      "s;\n      const double dt = softplus_f64(dr[t] + (bias ? bias[d] : 0.0));"),
     ("bwd_reverse_ignored", "(flags & ORACLE_REVERSE) ? (L - 1 - s) : s;\n          const double x = dr[t] + bd;",
      "s;\n          const double x = dr[t] + bd;"),
-    ("zoh_sign", "bbar = (abar - 1.0) / a_dn * Ab[n * L + t];", "bbar = (1.0 - abar) / a_dn * Ab[n * L + t];"),
+    ("zoh_sign", "bbar = expm1(dt * a_dn) / a_dn * Ab[n * L + t];", "bbar = -expm1(dt * a_dn) / a_dn * Ab[n * L + t];"),
     ("step_drops_u", "*h = abar * *h + bbar * u[r];", "*h = abar * *h + bbar;"),
-    ("A_transposed", "const double a_dn = A[d * N + n];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab",
-     "const double a_dn = A[n * Dm + d];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = (abar - 1.0) / a_dn * Ab"),
+    ("A_transposed", "const double a_dn = A[d * N + n];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = expm1(dt * a_dn) / a_dn * Ab",
+     "const double a_dn = A[n * Dm + d];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = expm1(dt * a_dn) / a_dn * Ab"),
     ("state_written_before_last_step", "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n];",
      "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n] * 0.5;"),
     ("step_bias_dropped", "const double dt = softplus_f64(delta[r] + (bias ? bias[d] : 0.0));",
@@ -59,7 +59,10 @@ MUTANTS = [
     ("bwd_zoh_e_dt_is_one", "const double e_dt = zoh ? a : 1.0;", "const double e_dt = 1.0;"),
     ("bwd_zoh_dA_term_dropped", "const double e_dA = !zoh ? 0.0 :", "const double e_dA = 1 ? 0.0 :"),
     ("bwd_zoh_dA_sign", "(dt * a - e) / an", "(e - dt * a) / an"),
-    ("bwd_zoh_dA_limit", "0.5 * dt * dt);", "dt * dt);"),
+    ("bwd_zoh_dA_limit", "double s = 0.0, f = 2.0, p = 1.0;", "double s = 0.0, f = 1.0, p = 1.0;"),
+    ("zoh_dA_closed_form_near_zero", "if (fabs(x) < 1e-2) {", "if (0) {"),
+    ("zoh_e_without_expm1", "bbar = expm1(dt * a_dn) / a_dn * Ab[n * L + t];",
+     "bbar = (exp(dt * a_dn) - 1.0) / a_dn * Ab[n * L + t];"),
     ("bwd_zoh_forward_euler", "const double h = a * hs[s * N + n] + e * Ab[n * L + t] * ur[t];",
      "const double h = a * hs[s * N + n] + dt * Ab[n * L + t] * ur[t];"),
     ("bwd_dz_silu_derivative", "sg * (1.0 + zr[t] * (1.0 - sg));", "sg;"),
