@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
 
     // per-(channel, step) values of this lane's 16 steps
     float dt[T], uu[T], xu[T], dy[T], dzf[T];
-    float cum = 0.0f, cumlo = 0.0f;
+    float cumlo = 0.0f, cumhi = 0.0f;  // step sizes of the lane's first and second half (kept apart:
+                                       // the second as a difference of sums would cancel)
 #pragma unroll
     for (int k = 0; k < T / EPC; ++k) {
       float fd[EPC], fu[EPC], fg[EPC], fz[EPC];
@@ -264,8 +265,8 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
           dzf[s] = 0.0f;
         }
         if (tv) dDacc = __builtin_fmaf(dy[s], fu[e], dDacc);
-        cum += dts;
-        if (s == T / 2 - 1) cumlo = cum;
+        if (s < T / 2) cumlo += dts;
+        else cumhi += dts;
       }
     }
 
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
             else Qb = __builtin_fmaf(a[s], Qb, bb);
           }
         }
-        const float Plo = exp2_(cumlo * A2), Phi = exp2_((cum - cumlo) * A2);
+        const float Plo = exp2_(cumlo * A2), Phi = exp2_(cumhi * A2);
         const float Pl = Plo * Phi;  // product of the lane's 16 decay factors
         float Q = __builtin_fmaf(Phi, Qa, Qb), P = Pl;
         row_scan_from_left(Q, P);

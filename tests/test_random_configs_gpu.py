@@ -142,3 +142,55 @@ def test_random_state_update(c):
         worst = max(worst, rel_err(y, ry), rel_err(st, ref_state))
     print("worst rel_err %.3g" % worst, flush=True)
     assert worst <= tol_for(torch.empty(0, dtype=dtype)), worst
+
+
+def _extreme_draws(n, seed=2024):
+    """Shapes, flags and value spreads, plus the seed of each case's tensors."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        c = dict(case=k, B=int(rng.integers(1, 3)), D=int(rng.integers(1, 40)),
+                 N=int(rng.choice([1, 4, 16, 17, 32, 64])), L=int(rng.choice([1, 7, 64, 129, 300, 2300])),
+                 zoh=bool(rng.integers(0, 2)), reverse=bool(rng.integers(0, 2)), seed=int(rng.integers(0, 1 << 30)))
+        c.update(u_scale=float(10 ** rng.uniform(-2, 2)), d_span=float(rng.uniform(1, 60)),
+                 d_shift=float(rng.uniform(0, 30)), b_scale=float(10 ** rng.uniform(-1, 1)),
+                 c_scale=float(10 ** rng.uniform(-1, 1)), skip=bool(rng.integers(0, 2)),
+                 gate=bool(rng.integers(0, 2)), bias=bool(rng.integers(0, 2)))
+        out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("c", _extreme_draws(80), ids=lambda c: "x%d" % c["case"])
+def test_random_extreme_values(c):
+    """Seeded shapes and flags with wide value distributions: A from -1e4 to -1e-6 with some
+    exact zeros, delta + bias up to +-30, u, B and C scaled over decades, the gate over
+    [-50, 50]; scan and backward in fp32 against the oracle."""
+    print("case:", c, flush=True)
+    B, D, N, L = c["B"], c["D"], c["N"], c["L"]
+    g = torch.Generator().manual_seed(c["seed"])
+    u = torch.randn(B, D, L, generator=g) * c["u_scale"]
+    delta = torch.rand(B, D, L, generator=g) * c["d_span"] - c["d_shift"]
+    A = -(10 ** (torch.rand(D, N, generator=g) * 10 - 6))
+    A[torch.rand(D, N, generator=g) < 0.1] = 0.0
+    Bm = torch.randn(B, N, L, generator=g) * c["b_scale"]
+    Cm = torch.randn(B, N, L, generator=g) * c["c_scale"]
+    Dv = torch.randn(D, generator=g) if c["skip"] else None
+    z = (torch.rand(B, D, L, generator=g) * 100 - 50) if c["gate"] else None
+    bias = torch.randn(D, generator=g) if c["bias"] else None
+    dout = torch.randn(B, D, L, generator=g)
+    dv = lambda t: None if t is None else t.float().to(DEV)
+    out, fs = scan_fwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), zoh=c["zoh"],
+                       reverse=c["reverse"])
+    gr = scan_bwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), dout=dv(dout), zoh=c["zoh"],
+                  reverse=c["reverse"])
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(u, delta, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, zoh=c["zoh"], reverse=c["reverse"])
+    ref = oracle.scan_bwd(u, delta, A, Bm, Cm, Dv, z, bias, None, dout=dout, dfinal=None, zoh=c["zoh"],
+                          reverse=c["reverse"])
+    errs = {"y": rel_err(out, ry), "state": rel_err(fs, rh)}
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias"):
+        if gr.get(k) is not None and ref.get(k) is not None:
+            errs[k] = rel_err(gr[k], ref[k])
+    print("rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()), flush=True)
+    bad = {k: e for k, e in errs.items() if not e <= 1e-4}
+    assert not bad, bad
