@@ -25,7 +25,8 @@
  *   dt     = softplus(x) = max(x,0) + log1p(exp(-|x|))
  *   Abar   = exp(dt * A[d,n])
  *   Bbar   = dt * B[b,n,t]                       (default)
- *          = (exp(dt*A) - 1) / A * B[b,n,t]      (ZOH flag; dt*B when A == 0)
+ *          = (exp(dt*A) - 1) / A * B[b,n,t]      (ZOH flag; dt*B when A == 0; evaluated as
+ *                                                expm1(dt*A) / A, which keeps its digits as dt*A -> 0)
  *   h[n]   = Abar * h[n] + Bbar * u[b,d,t]
  *   y      = sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]   (h after the update)
  *   out    = y * z / (1 + exp(-z))               (when z is given)
