@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from selective_state_space_76_amd import conv1d_fwd, scan_bwd, scan_fwd, state_update
+from selective_state_space_76_amd import checkpoints_shape, conv1d_fwd, scan_bwd, scan_fwd, state_update
 from selective_state_space_76_amd import workloads as W
 from tests.gpu_util import rel_err, tol_for
 
@@ -165,7 +165,18 @@ def test_random_extreme_values(c):
     """Seeded shapes and flags with wide value distributions: A from -1e4 to -1e-6 with some
     exact zeros, delta + bias up to +-30, u, B and C scaled over decades, the gate over
     [-50, 50]; scan and backward in fp32 against the oracle."""
-    print("case:", c, flush=True)
+    _check_extreme(c, boundary=False)
+
+
+@pytest.mark.parametrize("c", _extreme_draws(40, seed=2025), ids=lambda c: "s%d" % c["case"])
+def test_random_extreme_values_saved(c):
+    """The same value spreads with an initial state and a final-state gradient of random scale,
+    the forward keeping its block checkpoints and the backward starting from them."""
+    _check_extreme(c, boundary=True)
+
+
+def _check_extreme(c, boundary):
+    print("case:", c, "boundary/saved:", boundary, flush=True)
     B, D, N, L = c["B"], c["D"], c["N"], c["L"]
     g = torch.Generator().manual_seed(c["seed"])
     u = torch.randn(B, D, L, generator=g) * c["u_scale"]
@@ -178,19 +189,26 @@ def test_random_extreme_values(c):
     z = (torch.rand(B, D, L, generator=g) * 100 - 50) if c["gate"] else None
     bias = torch.randn(D, generator=g) if c["bias"] else None
     dout = torch.randn(B, D, L, generator=g)
+    h0 = dfin = ck = None
+    if boundary:
+        h0 = torch.randn(B, D, N, generator=g) * float(10 ** (torch.rand(1, generator=g) * 4 - 2))
+        dfin = torch.randn(B, D, N, generator=g) * float(10 ** (torch.rand(1, generator=g) * 4 - 2))
+        ck = torch.empty(checkpoints_shape(B, D, N, L), device=DEV)
     dv = lambda t: None if t is None else t.float().to(DEV)
-    out, fs = scan_fwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), zoh=c["zoh"],
-                       reverse=c["reverse"])
-    gr = scan_bwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), dout=dv(dout), zoh=c["zoh"],
-                  reverse=c["reverse"])
+    out, fs = scan_fwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), dv(h0), zoh=c["zoh"],
+                       reverse=c["reverse"], checkpoints=ck)
+    gr = scan_bwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), dv(h0), dout=dv(dout),
+                  dfinal_state=dv(dfin), zoh=c["zoh"], reverse=c["reverse"], checkpoints=ck)
     torch.cuda.synchronize()
-    ry, rh = oracle.scan(u, delta, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, zoh=c["zoh"], reverse=c["reverse"])
-    ref = oracle.scan_bwd(u, delta, A, Bm, Cm, Dv, z, bias, None, dout=dout, dfinal=None, zoh=c["zoh"],
+    ry, rh = oracle.scan(u, delta, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, h0=h0, zoh=c["zoh"],
+                         reverse=c["reverse"])
+    ref = oracle.scan_bwd(u, delta, A, Bm, Cm, Dv, z, bias, h0, dout=dout, dfinal=dfin, zoh=c["zoh"],
                           reverse=c["reverse"])
     errs = {"y": rel_err(out, ry), "state": rel_err(fs, rh)}
-    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias"):
-        if gr.get(k) is not None and ref.get(k) is not None:
-            errs[k] = rel_err(gr[k], ref[k])
+    for k, rk in [(k, k) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias")] + \
+            [("dinitial_state", "dh0")]:
+        if gr.get(k) is not None and ref.get(rk) is not None:
+            errs[k] = rel_err(gr[k], ref[rk])
     print("rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()), flush=True)
     bad = {k: e for k, e in errs.items() if not e <= 1e-4}
     assert not bad, bad
