@@ -227,14 +227,18 @@ def test_bwd_dB_dC_add_over_channel_halves():
 
 # The forward that saves its block checkpoints (ssm_scan_fwd_save) and the backward that starts
 # from them (ssm_scan_bwd_saved): the forward's outputs are unchanged, each checkpoint is the
-# oracle's state after the first 64 k steps, and the gradients match the oracle.
-@pytest.mark.parametrize("Bsz,Dm,N,L,zoh,reverse", [
-    (2, 24, 16, 300, False, False), (2, 24, 64, 300, True, True), (2, 20, 16, 7, False, True),
-    (1, 20, 16, 5000, False, False), (1, 20, 40, 5000, True, True), (1, 24, 64, 4100, False, True)],
-    ids=["16", "64zr", "short", "split16", "split40zr", "split64r"])
-def test_saved_checkpoints(Bsz, Dm, N, L, zoh, reverse):
-    print("case: saved checkpoints %dx%dx%dx%d zoh=%d reverse=%d f32" % (Bsz, Dm, N, L, zoh, reverse), flush=True)
-    x = make(Bsz, Dm, N, L, torch.float32, seed=11 * N + L, h0=True, dfin=True)
+# oracle's state after the first 64 k steps, and the gradients match the oracle and equal, bit for
+# bit, those of the backward that recomputes the checkpoints (both passes run the same recurrence).
+@pytest.mark.parametrize("Bsz,Dm,N,L,zoh,reverse,dtype", [
+    (2, 24, 16, 300, False, False, torch.float32), (2, 24, 64, 300, True, True, torch.float32),
+    (2, 20, 16, 7, False, True, torch.float32), (1, 20, 16, 5000, False, False, torch.float32),
+    (1, 20, 40, 5000, True, True, torch.float32), (1, 24, 64, 4100, False, True, torch.float32),
+    (2, 40, 16, 1000, False, False, torch.bfloat16), (1, 36, 64, 4500, True, False, torch.bfloat16)],
+    ids=["16", "64zr", "short", "split16", "split40zr", "split64r", "bf16", "split64z_bf16"])
+def test_saved_checkpoints(Bsz, Dm, N, L, zoh, reverse, dtype):
+    print("case: saved checkpoints %dx%dx%dx%d zoh=%d reverse=%d %s" % (Bsz, Dm, N, L, zoh, reverse, dtype),
+          flush=True)
+    x = make(Bsz, Dm, N, L, dtype, seed=11 * N + L, h0=True, dfin=True)
     d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
     args = (d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], d["h0"])
     ck = torch.full(checkpoints_shape(Bsz, Dm, N, L), float("nan"), device=DEV)
@@ -267,3 +271,4 @@ def test_saved_checkpoints(Bsz, Dm, N, L, zoh, reverse):
           % same, flush=True)
     bad = {k: e for k, e in errs.items() if not e <= tol}
     assert not bad, bad
+    assert same, "the saving forward's checkpoints differ from the checkpoint pass's"
