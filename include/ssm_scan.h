@@ -36,6 +36,9 @@
  *   - `out` and `final_state` must not overlap any input (checked: SSM_ERR_OVERLAP).
  *   - Calls are reentrant; concurrent calls on different streams are safe when
  *     their output buffers are distinct.
+ *   - Indexing is 64-bit: a tensor may hold more than 2^31 elements.
+ *   - Arithmetic is fp32 with denormals flushed: a result whose exact magnitude
+ *     is below about 1e-36 may come back as 0.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
