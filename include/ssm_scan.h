@@ -37,8 +37,8 @@
  *   - Calls are reentrant; concurrent calls on different streams are safe when
  *     their output buffers are distinct.
  *   - Indexing is 64-bit: a tensor may hold more than 2^31 elements.
- *   - Arithmetic is fp32 with denormals flushed: a result whose exact magnitude
- *     is below about 1e-36 may come back as 0.
+ *   - Arithmetic is fp32: a result whose exact magnitude is below about 1e-36
+ *     (near or under fp32's smallest normal number) may come back as 0.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
