@@ -164,6 +164,10 @@ __device__ __forceinline__ void load_piece(const IO* row, int64_t ts, int64_t L,
   }
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// outstanding global loads and stores (the waves of a workgroup exchange data through LDS only).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace bwdc
 
 template <typename IO, int T, bool ZOH, bool REV, bool VEC>
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
     for (int s = 0; s < T; ++s) { yv[s] = 0.0f; S1[s] = 0.0f; S2[s] = 0.0f; }
 
     for (int64_t n0 = 0; n0 < N; n0 += 16) {
-      __syncthreads();  // every wave is done with the previous stage's tile
+      lds_barrier();  // every wave is done with the previous stage's tile
       // the checkpointed states entering the chunk, one (channel tid / 16, state n0 + tid % 16) per
       // thread, loaded with the tile so that no state waits on a global load
       float hcv = 0.0f;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         }
       }
       hck[tid] = hcv;
-      __syncthreads();
+      lds_barrier();
 
       const int ng = (N - n0) < 16 ? (int)(N - n0) : 16;
 #pragma unroll 1
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         if (g == 0) da[n] += dAl;
 
         // dB, dC over the workgroup's 16 channels: the 4 waves' row sums through LDS, in wave order
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int e = tid; e < 2 * CH; e += 256) {
           const int qty = e / CH, step = e % CH;
