@@ -133,6 +133,17 @@ def _stream(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(stream, *tensors):
+    """Tensors this module allocated are taken from torch's current stream; when the kernels run
+    on another stream, tell the caching allocator so the memory is not handed out again before
+    that stream's work on it is done."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def make_shape(batch, dim, dstate, seqlen, io_dtype, zoh=False, reverse=False) -> ssm_shape:
     flags = (SSM_FLAG_ZOH if zoh else 0) | (SSM_FLAG_REVERSE if reverse else 0)
     return ssm_shape(int(batch), int(dim), int(dstate), int(seqlen), int(io_dtype), flags)
@@ -166,10 +177,13 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     io = _io_dtype(u)
     device = u.device
     sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
+    made = []  # tensors allocated here (on torch's current stream)
     if out is None:
         out = torch.empty_like(u)
+        made.append(out)
     if final_state is True:
         final_state = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=u.device)
+        made.append(final_state)
     elif final_state is False:
         final_state = None
     f32 = torch.float32
@@ -189,6 +203,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
         need = int(lib.ssm_scan_workspace_size(ctypes.byref(sh)))
         if need and workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+            made.append(workspace)
         if workspace is not None:
             ws_bytes = workspace.numel() * workspace.element_size()
     else:
@@ -201,6 +216,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
         _check(lib.ssm_scan_fwd_save(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                      _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
                                      _ptr(checkpoints), _ptr(workspace), ws_bytes, _stream(stream, device)))
+    _on_stream(stream, *made)
     return out, final_state
 
 
@@ -214,8 +230,10 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     _nonempty(batch=Bsz, dim=Dm, dstate=N)
     io = _io_dtype(u)
     device = u.device
+    made = []
     if out is None:
         out = torch.empty_like(u)
+        made.append(out)
     f32 = torch.float32
     for t, shp, dt, name in ((state, (Bsz, Dm, N), f32, "state"), (delta, (Bsz, Dm), u.dtype, "delta"),
                              (A, (Dm, N), f32, "A"), (B, (Bsz, N), u.dtype, "B"), (C, (Bsz, N), u.dtype, "C"),
@@ -225,6 +243,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     _check(lib.ssm_state_update(Bsz, Dm, N, io, SSM_FLAG_ZOH if zoh else 0, _ptr(state), _ptr(u), _ptr(delta),
                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
                                 _stream(stream, device)))
+    _on_stream(stream, *made)
     return out
 
 
@@ -265,12 +284,14 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                   dB=((Bsz, N, L), f32), dC=((Bsz, N, L), f32), dD=((Dm,), f32),
                   dz=((Bsz, Dm, L), u.dtype), ddelta_bias=((Dm,), f32), dinitial_state=((Bsz, Dm, N), f32))
     g = dict(grads or {})
+    made = []
     for k, (shp, dt) in shapes.items():
         if k == "dz" and z is None:
             g[k] = None
             continue
         if g.get(k) is None:
             g[k] = torch.empty(shp, dtype=dt, device=dev)
+            made.append(g[k])
         _expect(g[k], shp, dt, k, device)
     size_fn = lib.ssm_scan_bwd_workspace_size if checkpoints is None else lib.ssm_scan_bwd_saved_workspace_size
     need = int(size_fn(ctypes.byref(sh)))
@@ -278,6 +299,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
         raise ValueError("workspace: expected a tensor on %s, got %s" % (device, workspace.device))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     outs = (_ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]))
@@ -288,6 +310,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     else:
         _check(lib.ssm_scan_bwd_saved(ctypes.byref(sh), *ins, _ptr(checkpoints), *outs, _ptr(workspace), ws_bytes,
                                       _stream(stream, device)))
+    _on_stream(stream, *made)
     return g
 
 
@@ -302,10 +325,13 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_stat
     _nonempty(batch=Bsz, dim=Dm, seqlen=L, width=K)
     io = _io_dtype(x)
     device = x.device
+    made = []
     if out is None:
         out = torch.empty_like(x)
+        made.append(out)
     if final_state is True:
         final_state = torch.empty((Bsz, Dm, K - 1), dtype=x.dtype, device=x.device)
+        made.append(final_state)
     elif final_state is False:
         final_state = None
     f32 = torch.float32
@@ -316,6 +342,7 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, *, out=None, final_stat
         _expect(t, shp, dt, name, device)
     _check(lib.ssm_conv1d_fwd(Bsz, Dm, L, K, io, _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state),
                               _ptr(out), _ptr(final_state), _stream(stream, device)))
+    _on_stream(stream, *made)
     return out, final_state
 
 
@@ -328,8 +355,10 @@ def conv1d_update(conv_state, x, weight, bias=None, *, out=None, stream=None):
     _nonempty(batch=Bsz, dim=Dm, width=K)
     io = _io_dtype(x)
     device = x.device
+    made = []
     if out is None:
         out = torch.empty_like(x)
+        made.append(out)
     f32 = torch.float32
     for t, shp, dt, name in ((conv_state, (Bsz, Dm, K - 1), x.dtype, "conv_state"),
                              (weight, (Dm, K), f32, "weight"), (bias, (Dm,), f32, "bias"),
@@ -337,4 +366,5 @@ def conv1d_update(conv_state, x, weight, bias=None, *, out=None, stream=None):
         _expect(t, shp, dt, name, device)
     _check(lib.ssm_conv1d_update(Bsz, Dm, K, io, _ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias),
                                  _ptr(out), _stream(stream, device)))
+    _on_stream(stream, *made)
     return out

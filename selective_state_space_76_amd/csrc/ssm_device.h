@@ -333,6 +333,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
 
   fetch(tb);
   if (NBUF == 2) {  // block 0 goes straight into buffer 0; block 1 streams in during block 0
+    __syncthreads();  // every thread's share of the zero fill lands before any chunk is stored
     store(tiles);
     fetch(tb + 64);
   }

@@ -227,14 +227,52 @@ def check_single_step_closed_form(orc):
 
 
 def check_step_matches_scan(orc):
-    inp = tiny_inputs(71, L=20)
-    y, h = orc.scan(**inp)
-    st = np.zeros((2, 3, 4))
-    for t in range(20):
-        yt, st = orc.step(st, inp["u"][..., t], inp["delta"][..., t], inp["A"], inp["B"][..., t],
-                          inp["C"][..., t], D=inp["D"], z=inp["z"][..., t], delta_bias=inp["delta_bias"])
-        assert rel(yt, y[..., t]) < 1e-14
-    assert rel(st, h) < 1e-14
+    """scan(L) equals L single steps, in both discretisations (the scan's ZOH is pinned to
+    scipy's cont2discrete and to 60-digit decimal arithmetic near A = 0, so this carries those
+    pins over to the step); decays from the workload range and from next to A = 0."""
+    for zoh in (False, True):
+        for near_zero in (False, True):
+            inp = tiny_inputs(71 + 2 * zoh + near_zero, L=20)
+            if near_zero:
+                inp["A"] = -np.logspace(-7, -3, inp["A"].size).reshape(inp["A"].shape)
+            y, h = orc.scan(**inp, zoh=zoh)
+            st = np.zeros((2, 3, 4))
+            for t in range(20):
+                yt, st = orc.step(st, inp["u"][..., t], inp["delta"][..., t], inp["A"], inp["B"][..., t],
+                                  inp["C"][..., t], D=inp["D"], z=inp["z"][..., t],
+                                  delta_bias=inp["delta_bias"], zoh=zoh)
+                assert rel(yt, y[..., t]) < 1e-14, (zoh, near_zero, t)
+            assert rel(st, h) < 1e-14, (zoh, near_zero)
+
+
+def check_step_zoh_closed_form(orc):
+    """One ZOH step by hand: delta + bias = 0 gives dt = ln 2 and A = -1 gives A_bar = 1/2, so
+    B_bar = (A_bar - 1) / A * B = B / 2 (freeguideonline tutorial, section 2.2).  From h = 3 with
+    B = 4, u = 1.5: h' = 3/2 + 2 * 1.5 = 4.5, and y = C h' = 9 for C = 2.  Then a general step
+    against scipy's cont2discrete (zoh) of the one-state system (A, B) at that step size, and
+    the step next to A = 0 against its closed form in 60-digit decimal arithmetic."""
+    from decimal import Decimal, getcontext
+    one = np.ones((1, 1))
+    y, st = orc.step(np.full((1, 1, 1), 3.0), 1.5 * one, 0.0 * one, -one, 4.0 * one, 2.0 * one, zoh=True)
+    assert abs(st[0, 0, 0] - 4.5) < 1e-15 and abs(y[0, 0] - 9.0) < 1e-14, (st, y)
+    rng = np.random.default_rng(77)
+    for _ in range(5):
+        a, bq, x, u0, h0 = -rng.uniform(0.05, 4.0), rng.standard_normal(), rng.uniform(-2, 1), \
+            rng.standard_normal(), rng.standard_normal()
+        dt = float(_softplus(x))
+        Ad, Bd, _, _, _ = scipy.signal.cont2discrete((np.array([[a]]), np.array([[bq]]), np.ones((1, 1)),
+                                                      np.zeros((1, 1))), dt, method="zoh")
+        _, st = orc.step(np.full((1, 1, 1), h0), u0 * one, x * one, a * one, bq * one, one, zoh=True)
+        want = Ad[0, 0] * h0 + Bd[0, 0] * u0
+        assert abs(st[0, 0, 0] - want) < 1e-12 * max(1.0, abs(want)), (a, st[0, 0, 0], want)
+    getcontext().prec = 60
+    x, u0, bq = 0.4, 1.3, 0.6
+    dt = float(np.logaddexp(0.0, x))
+    for a in (-1e-6, 3e-7, -2e-3, -0.05):
+        _, st = orc.step(np.zeros((1, 1, 1)), u0 * one, x * one, a * one, bq * one, one, zoh=True)
+        D_dt, D_A = Decimal(dt), Decimal(a)
+        want = float(((D_dt * D_A).exp() - 1) / D_A * Decimal(bq) * Decimal(u0))
+        assert abs(st[0, 0, 0] - want) <= 1e-14 * abs(want), (a, st[0, 0, 0], want)
 
 
 def check_softplus_silu(orc):
@@ -542,7 +580,7 @@ def check_zoh_near_zero_decay_exact(orc):
 
 ALL_CHECKS = [check_brute_force, check_initial_state, check_lti_closed_form, check_zoh_library,
               check_a_zero_cumsum, check_small_step_skip, check_single_step_closed_form,
-              check_step_matches_scan, check_softplus_silu, check_linearity_in_u, check_causality,
+              check_step_matches_scan, check_step_zoh_closed_form, check_softplus_silu, check_linearity_in_u, check_causality,
               check_reverse, check_permutation_equivariance,
               check_conv_library, check_conv_impulse, check_conv_k1, check_conv_state_out,
               check_conv_chunking, check_conv_causality,

@@ -36,6 +36,12 @@ MUTANTS = [
      "const double a_dn = A[n * Dm + d];\n        const double abar = exp(dt * a_dn);\n        double bbar;\n        if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n          bbar = expm1(dt * a_dn) / a_dn * Ab"),
     ("state_written_before_last_step", "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n];",
      "for (int64_t n = 0; n < N; ++n) final_state[r * N + n] = h[n] * 0.5;"),
+    ("step_zoh_sign", "bbar = expm1(dt * a_dn) / a_dn * Bm[b * N + n];",
+     "bbar = -expm1(dt * a_dn) / a_dn * Bm[b * N + n];"),
+    ("step_zoh_without_expm1", "bbar = expm1(dt * a_dn) / a_dn * Bm[b * N + n];",
+     "bbar = (exp(dt * a_dn) - 1.0) / a_dn * Bm[b * N + n];"),
+    ("step_zoh_ignored", "if ((flags & ORACLE_ZOH) && a_dn != 0.0)\n        bbar = expm1(dt * a_dn) / a_dn * Bm",
+     "if (0)\n        bbar = expm1(dt * a_dn) / a_dn * Bm"),
     ("step_bias_dropped", "const double dt = softplus_f64(delta[r] + (bias ? bias[d] : 0.0));",
      "const double dt = softplus_f64(delta[r]);"),
     ("conv_taps_flipped", "v += w[d * K + k] * xe[t + k];", "v += w[d * K + (K - 1 - k)] * xe[t + k];"),
