@@ -62,7 +62,8 @@ typedef enum ssm_status {
   SSM_ERR_UNSUPPORTED = 5, /* unknown flag bits */
   SSM_ERR_WORKSPACE = 6,   /* workspace non-NULL but smaller than ssm_scan_workspace_size() */
   SSM_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch (hipGetLastError) */
-  SSM_ERR_OVERLAP = 8      /* an output buffer overlaps an input buffer */
+  SSM_ERR_OVERLAP = 8,     /* an output buffer overlaps an input buffer */
+  SSM_ERR_TOO_LARGE = 9    /* ssm_scan_fwd_noalloc: the shape needs more than its 8 MiB of scratch */
 } ssm_status;
 
 typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -134,6 +135,28 @@ ssm_status ssm_scan_fwd_save(const ssm_shape* shape,
                              void* out, float* final_state, float* checkpoints,
                              void* workspace, size_t workspace_bytes,
                              struct ihipStream_t* stream);
+
+/* ssm_scan_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): it takes no workspace
+ * and allocates nothing.  A sequence split uses a scratch array of 8 MiB that the
+ * library holds in static device memory, one copy per GPU, kept until the process
+ * ends; its address is looked up once per device, on the first call there.
+ *   - Arguments, outputs and errors are those of ssm_scan_fwd, with the split always
+ *     enabled; a shape whose split needs more than 8 MiB (ssm_scan_workspace_size()
+ *     > 8 MiB) is refused with SSM_ERR_TOO_LARGE before anything is enqueued.
+ *   - `stream` must belong to the device whose scratch is used (its own device).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *     contents: calls that overlap in time on one GPU (on different streams, or
+ *     from different host threads without ordering) race on it and give undefined
+ *     results.  Serialise them, e.g. on one stream.
+ * Results are bitwise those of ssm_scan_fwd with a workspace. */
+ssm_status ssm_scan_fwd_noalloc(const ssm_shape* shape,
+                                const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D,
+                                const void* z, const float* delta_bias,
+                                const float* initial_state,
+                                void* out, float* final_state,
+                                struct ihipStream_t* stream);
 
 /* One recurrent generation step (the scan body with L = 1), state updated in place:
  * the fixed-size state replaces a growing cache (fsdata.site article, section 3.2

@@ -20,7 +20,8 @@ SSM_FLAG_REVERSE = 2
 ABI_VERSION = 2
 
 _STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_ALIGN",
-           5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH", 8: "SSM_ERR_OVERLAP"}
+           5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH", 8: "SSM_ERR_OVERLAP",
+           9: "SSM_ERR_TOO_LARGE"}
 
 
 class SSMError(RuntimeError):
@@ -36,6 +37,7 @@ class ssm_shape(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("ssm_abi_version", "ssm_status_str", "ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_save",
+           "ssm_scan_fwd_noalloc",
            "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_scan_bwd_saved_workspace_size",
            "ssm_scan_bwd_saved", "ssm_conv1d_fwd", "ssm_conv1d_update")
 
@@ -60,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_save.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 12 + [vp, ctypes.c_size_t, vp]
     lib.ssm_scan_fwd_save.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ssm_shape)] + [vp] * 11 + [vp]
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, u32] + [vp] * 10 + [vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ssm_shape)]
@@ -217,6 +221,37 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
                                      _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
                                      _ptr(checkpoints), _ptr(workspace), ws_bytes, _stream(stream, device)))
     _on_stream(stream, *made)
+    return out, final_state
+
+
+SCRATCH_BYTES = 8 << 20  # the static scratch array behind ssm_scan_fwd_noalloc
+
+
+def scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *, out, final_state=None,
+                     zoh=False, reverse=False, stream=None):
+    """ssm_scan_fwd_noalloc: the selective scan without a workspace; the library's static 8 MiB
+    per-device scratch array holds a split sequence's segment summaries, and the call allocates
+    nothing.  out (and final_state, if given) are the caller's tensors; arguments as scan_fwd.
+    Calls that overlap in time on one GPU race on the shared scratch."""
+    lib = load()
+    Bsz, Dm, L = u.shape
+    N = A.shape[1]
+    _nonempty(batch=Bsz, dim=Dm, dstate=N, seqlen=L)
+    io = _io_dtype(u)
+    device = u.device
+    sh = make_shape(Bsz, Dm, N, L, io, zoh, reverse)
+    f32 = torch.float32
+    for t, shp, dt, name in ((delta, (Bsz, Dm, L), u.dtype, "delta"), (A, (Dm, N), f32, "A"),
+                             (B, (Bsz, N, L), u.dtype, "B"), (C, (Bsz, N, L), u.dtype, "C"),
+                             (D, (Dm,), f32, "D"), (z, (Bsz, Dm, L), u.dtype, "z"),
+                             (delta_bias, (Dm,), f32, "delta_bias"),
+                             (initial_state, (Bsz, Dm, N), f32, "initial_state"),
+                             (out, (Bsz, Dm, L), u.dtype, "out"),
+                             (final_state, (Bsz, Dm, N), f32, "final_state")):
+        _expect(t, shp, dt, name, device)
+    _check(lib.ssm_scan_fwd_noalloc(ctypes.byref(sh), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(delta_bias), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                    _stream(stream, device)))
     return out, final_state
 
 

@@ -2,7 +2,8 @@
 //
 // Every argument is validated on the host before anything is enqueued; no HIP
 // runtime call is made for an invalid call, so the checks can be exercised on
-// a machine without a GPU.  The library allocates no memory and keeps no state.
+// a machine without a GPU.  The library allocates no memory; its only state is the
+// per-device address of the static scratch array of ssm_scan_fwd_noalloc.
 #include <stdint.h>
 #include <string.h>
 
@@ -157,6 +158,7 @@ const char* ssm_status_str(int status) {
     case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_workspace_size()";
     case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SSM_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (8 MiB)";
     default: return "unknown status";
   }
 }
@@ -177,7 +179,7 @@ ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delt
                          const void* B, const void* C, const float* D, const void* z,
                          const float* delta_bias, const float* initial_state, void* out,
                          float* final_state, float* ckpt, void* workspace, size_t workspace_bytes,
-                         struct ihipStream_t* stream) {
+                         struct ihipStream_t* stream, bool use_scratch = false) {
   if (!shape) return SSM_ERR_NULL;
   if (shape->io_dtype != SSM_F32 && shape->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (shape->flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE)) return SSM_ERR_UNSUPPORTED;
@@ -208,10 +210,12 @@ ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delt
     if (overlaps(rc_, r)) return SSM_ERR_OVERLAP;
   if (overlaps(rc_, ro) || overlaps(rc_, rf)) return SSM_ERR_OVERLAP;
 
-  const bool split = pl.S > 1 && workspace != nullptr;
-  if (pl.S > 1 && workspace != nullptr && workspace_bytes < pl.total) return SSM_ERR_WORKSPACE;
-  if (pl.S > 1 && workspace == nullptr && workspace_bytes != 0) return SSM_ERR_NULL;
-  if (split) {
+  // use_scratch: the split runs in the library's static per-device array (ssm_scan_fwd_noalloc)
+  const bool split = pl.S > 1 && (workspace != nullptr || use_scratch);
+  if (use_scratch && pl.total > ssm::kScratchBytes) return SSM_ERR_TOO_LARGE;
+  if (!use_scratch && pl.S > 1 && workspace != nullptr && workspace_bytes < pl.total) return SSM_ERR_WORKSPACE;
+  if (!use_scratch && pl.S > 1 && workspace == nullptr && workspace_bytes != 0) return SSM_ERR_NULL;
+  if (split && !use_scratch) {
     const Range rw = span(workspace, (int64_t)pl.total, 1);
     for (const Range& r : ins)
       if (overlaps(rw, r)) return SSM_ERR_OVERLAP;
@@ -234,6 +238,9 @@ ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delt
     p.S = 1;
     p.seg_len = ((L + 63) / 64) * 64;
     return launch_status(ssm::launch_scan(p, bf16, 0, st));
+  }
+  if (use_scratch) {  // every argument has been checked; now the device address of the array
+    if (ssm::scratch_buffer(st, &workspace) != hipSuccess) return SSM_ERR_LAUNCH;
   }
   char* ws = static_cast<char*>(workspace);
   p.S = (int)pl.S;
@@ -270,6 +277,14 @@ ssm_status ssm_scan_fwd_save(const ssm_shape* shape, const void* u, const void* 
   if (!checkpoints) return SSM_ERR_NULL;
   return scan_fwd_impl(shape, u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, checkpoints,
                        workspace, workspace_bytes, stream);
+}
+
+ssm_status ssm_scan_fwd_noalloc(const ssm_shape* shape, const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const float* initial_state, void* out,
+                                float* final_state, struct ihipStream_t* stream) {
+  return scan_fwd_impl(shape, u, delta, A, B, C, D, z, delta_bias, initial_state, out, final_state, nullptr,
+                       nullptr, 0, stream, true);
 }
 
 ssm_status ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int32_t io_dtype, uint32_t flags,

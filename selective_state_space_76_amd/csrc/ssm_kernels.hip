@@ -1,7 +1,45 @@
-// ssm_kernels.hip -- launchers: scan dispatch, carry pass and the decode step.
+// ssm_kernels.hip -- launchers: scan dispatch, carry pass and the decode step; the scratch
+// memory of the entry point that allocates nothing.
+#include <mutex>
+
 #include "ssm_device.h"
 
 namespace ssm {
+
+// Scratch memory of ssm_scan_fwd_noalloc: a file-scope device array, so the call needs no
+// allocation.  Each GPU the library runs on holds its own copy, at its own address, until the
+// process ends.  In host code the name `scratch` is only a stand-in for the symbol; its device
+// address comes from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_buffer(hipStream_t stream, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {  // the device the work will run on
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;  // the symbol of that device
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // Chains the segment summaries: carries[s] is the state entering segment s.
 __global__ __launch_bounds__(256) void carry_kernel(ScanParams p) {

@@ -107,4 +107,10 @@ hipError_t launch_adj_carry(const BwdParams& p, float* adj_in, hipStream_t s);
 hipError_t launch_reduce(float* out, const float* part, int64_t count, int64_t stride, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
 
+// Size of the static per-device scratch array behind ssm_scan_fwd_noalloc, and its device address
+// on the device `stream` belongs to (the current device for the null stream), looked up once per
+// device.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+hipError_t scratch_buffer(hipStream_t stream, void** ptr);
+
 }  // namespace ssm

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = L.load()
-    for s in range(9):
-        assert lib.ssm_status_str(s)
+    for s in range(10):
+        assert lib.ssm_status_str(s) and lib.ssm_status_str(s) != b"unknown status"
     assert lib.ssm_status_str(12345) == b"unknown status"
 
 
@@ -280,3 +280,27 @@ def test_saved_checkpoint_entry_points():
     S, bdn, bd = 5, 320, 20
     assert (lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) - lib.ssm_scan_bwd_saved_workspace_size(ctypes.byref(s))
             == r(4 * bdn * ((5000 + 63) // 64)) + r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn))
+
+
+def test_noalloc_errors_before_any_launch():
+    """ssm_scan_fwd_noalloc checks every argument on the host first, then its scratch limit (a
+    split that needs more than its 8 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
+    lib = L.load()
+
+    def call(shape, **kw):
+        p = good_ptrs()
+        p.update(kw)
+        return lib.ssm_scan_fwd_noalloc(None if shape is None else ctypes.byref(shape), p["u"], p["delta"], p["A"],
+                                        p["B"], p["C"], None, None, None, None, p["out"], None, None)
+
+    big = shp(batch=1, dim=8000, dstate=64, seqlen=4096)
+    assert L.load().ssm_scan_workspace_size(ctypes.byref(big)) > L.SCRATCH_BYTES
+    assert call(big) == 9
+    assert call(None) == 1
+    assert call(shp(dstate=65)) == 2
+    assert call(shp(io_dtype=7)) == 3
+    assert call(shp(), u=None) == 1
+    assert call(shp(), B=fake(4, 8)) == 4
+    assert call(shp(flags=8)) == 5
+    assert call(shp(), out=fake(1)) == 8  # out is u
+    assert call(big, out=fake(1)) == 8    # argument errors come before the scratch limit
