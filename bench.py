@@ -1,24 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the MI355X selective scan (one GPU).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba130m]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dna1m]
 
 A step is one ssm_scan_fwd call over a whole batch of the workload (discretise,
-scan, carry, output epilogue: the entire prefill/training-forward path) with
-every input already resident in HBM.  The timed loop rotates through enough
-independent input sets that they cannot be served from the 256 MB Infinity
-Cache.  The same JSON line also carries the decode path (ssm_state_update) on
-the 2.8B-shaped generation workload, the backward pass (ssm_scan_bwd; as context
-also its ZOH variant and ssm_scan_bwd_saved from a saving forward's checkpoints) on
-the same workload, the conv + SiLU step that produces u
-(ssm_conv1d_fwd on the same [B, D, L] shape, ssm_conv1d_update on the decode
-shape) and the fp64 CPU oracle's rate on the host.
+scan, carry across sequence segments, output epilogue: the entire
+prefill/training-forward path) with every input already resident in HBM.  The
+headline workload is the largest configuration, the million-step DNA-like
+sequence (1 x 1024 channels x 16 states x 1,048,576 steps); the 130M- and
+1.3B-shaped layer scans are measured the same way as sub-records.  Inputs are
+rotated through enough independent sets that they cannot be served from the
+256 MB Infinity Cache.  The same JSON line carries the decode path
+(ssm_state_update) on the 2.8B-shaped generation workload, the backward pass
+(ssm_scan_bwd) on the two layer shapes, the conv + SiLU step that produces u,
+a probe of the VALU issue rate, and the fp64 CPU oracle's rate on a bounded
+sample of the headline workload.
 
 Progress goes to stderr; stdout gets exactly one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -29,14 +32,18 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "selective-scan state updates/sec (B·L·D·N) and HBM GB/s % of peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-# ALU roofline of the scan.  A state update needs, at minimum, 5 fp32 operations: the exp2
-# argument (mul), exp2 (v_exp_f32), B_bar*u (mul), the state update (FMA) and C*h (FMA).
-# Measured issue cost on gfx950 with >= 2 waves per SIMD (two waves issue VALU concurrently):
-# 1.9 clk per wave64 plain fp32 op and 5.5 clk per v_exp_f32.  The peak rate of this op mix is
-# 5 ops per (4 * 1.9 + 5.5) clk per 64 lanes per SIMD, over 1024 SIMDs at 2.4 GHz.
-OPS_PER_UPDATE = 5
-ALU_PEAK_TOPS = OPS_PER_UPDATE * 64 / (4 * 1.9 + 5.5) * 1024 * 2.4e9 / 1e12
+# Published MI355X fp32 vector peak (it counts packed two-per-lane FMAs; see alu_issue_probe).
+FP32_PEAK_TFLOPS = 157.3
+# Algorithmic fp32 work of one forward state update: the exp2 argument (mul), exp2, B_bar * u
+# (mul), the state update (FMA) and C * h (FMA); multiplies and the exp count 1, FMAs 2.
+FLOPS_PER_UPDATE = 7
+# Backward, per state update: restore the state (exp argument, exp, B_bar * u, FMA: 5); the adjoint
+# G = G * A_bar + dy * C (mul + FMA: 3); dC += dy * h and dB += G * dt * u, each a product added
+# over channels (2 + 2); sum_n G * B (FMA: 2); p = h_prev * A_bar, q = G * p, ddt += q * A (FMA),
+# dA += q * dt (FMA) (1 + 1 + 2 + 2).
+BWD_FLOPS_PER_UPDATE = 20
 MALL_BYTES = 256 << 20
+SUB_CONFIGS = ("mamba130m", "mamba1p3b")
 
 
 def log(*a):
@@ -80,8 +87,10 @@ def traffic_from_profile(workload: str, launches_per_call: int):
     return c.get("hbm_bytes_per_launch")
 
 
-def bench_scan(args, torch, ssm, W):
-    w = W.WORKLOADS[args.workload]
+def scan_record(args, torch, ssm, W, name, steps, warmup, keep_inputs=False):
+    """Time ssm_scan_fwd on one workload: events around every call on the launch stream (torch's
+    current stream), wall time over all calls.  Returns the record (and the first input set)."""
+    w = W.WORKLOADS[name]
     per_set = scan_bytes(w)
     R = max(1, min(8, math.ceil(2 * MALL_BYTES / per_set)))
     log("workload %s %s, %d rotated input sets of %.1f MB" % (w.name, (w.batch, w.dim, w.dstate, w.seqlen),
@@ -92,43 +101,66 @@ def bench_scan(args, torch, ssm, W):
         x["out"] = torch.empty_like(x["u"])
         x["fs"] = torch.empty(w.batch, w.dim, w.dstate, device="cuda")
         sets.append(x)
-    need = ssm.workspace_size(w.batch, w.dim, w.dstate, w.seqlen, ssm.SSM_BF16 if w.io == "bf16" else ssm.SSM_F32)
+    io = ssm.SSM_BF16 if w.io == "bf16" else ssm.SSM_F32
+    need = ssm.workspace_size(w.batch, w.dim, w.dstate, w.seqlen, io)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
 
     def call(x):
         ssm.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                      out=x["out"], final_state=x["fs"], workspace=ws)
 
-    for k in range(args.warmup):
+    for k in range(warmup):
         call(sets[k % R])
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         starts[k].record()
         call(sets[k % R])
         ends[k].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    mean_launch = sum(launch_ms) / len(launch_ms)
-    # the same launch with L2 and the Infinity Cache flushed before each rep (a 1 GiB fill outside
-    # the events), as a cross-check of the rotation above
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    nf = min(args.steps, 20)
-    fs_, fe_ = [torch.cuda.Event(enable_timing=True) for _ in range(nf)], [torch.cuda.Event(enable_timing=True) for _ in range(nf)]
-    for k in range(nf):
-        flush.zero_()
-        fs_[k].record()
-        call(sets[k % R])
-        fe_[k].record()
-    torch.cuda.synchronize()
-    flushed = sorted(s_.elapsed_time(e_) for s_, e_ in zip(fs_, fe_))
-    del flush
-    return w, R, ms_step, mean_launch, launch_ms, sets[0], flushed
+    launch = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+    ms_step = (t1 - t0) * 1e3 / steps
+    mean = sum(launch) / len(launch)
+    rec = {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen,
+           "io_dtype": w.io, "rotated_input_sets": R, "steps": steps, "ms_per_step": ms_step,
+           "value": w.updates / (ms_step * 1e-3), "unit": "state-updates/s",
+           "call_ms": mean, "call_ms_median": launch[len(launch) // 2],
+           "call_ms_p10": launch[len(launch) // 10], "call_ms_p90": launch[(9 * len(launch)) // 10],
+           "workspace_bytes": need}
+    if R > 1 and per_set <= MALL_BYTES:
+        # the same call with L2 and the Infinity Cache flushed before each rep (a 1 GiB fill outside
+        # the events), as a cross-check of the rotation above
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        nf = min(steps, 20)
+        fs_ = [torch.cuda.Event(enable_timing=True) for _ in range(nf)]
+        fe_ = [torch.cuda.Event(enable_timing=True) for _ in range(nf)]
+        for k in range(nf):
+            flush.zero_()
+            fs_[k].record()
+            call(sets[k % R])
+            fe_[k].record()
+        torch.cuda.synchronize()
+        flushed = sorted(a.elapsed_time(b) for a, b in zip(fs_, fe_))
+        del flush
+        rec["flushed_call_ms_median"] = flushed[len(flushed) // 2]
+    flops = w.updates * FLOPS_PER_UPDATE / (mean * 1e-3) / 1e12
+    b = scan_bytes(w)
+    gbs = b / (mean * 1e-3) / 1e9
+    rec["roofline"] = {"bound": "alu", "achieved": flops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": flops / FP32_PEAK_TFLOPS, "traffic": traffic_from_profile(w.name, 1),
+                       "flops_per_update": FLOPS_PER_UPDATE, "algorithmic_flops_per_call": w.updates * FLOPS_PER_UPDATE,
+                       "call_ms": mean}
+    rec["hbm"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                  "algorithmic_bytes_per_call": b}
+    log("scan %s: %.4f ms/step (wall), %.4f ms/call (events) -> %.3e updates/s, %.2f TFLOP/s, %.1f GB/s"
+        % (w.name, ms_step, mean, rec["value"], flops, gbs))
+    x0 = sets[0] if keep_inputs else None
+    del sets, ws
+    return rec, w, x0
 
 
 def bench_decode(args, torch, ssm, W):
@@ -228,10 +260,10 @@ def bwd_bytes(w) -> int:
             + 4 * 4 * w.dim)
 
 
-def bench_bwd(args, torch, ssm, W):
-    """One ssm_scan_bwd call per step on the scan workload (checkpoint pass, backward pass and
+def bench_bwd(args, torch, ssm, W, name):
+    """One ssm_scan_bwd call per step on a layer workload (checkpoint pass, backward pass and
     the fixed-order partial sums), inputs rotated past the Infinity Cache."""
-    w = W.WORKLOADS[args.workload]
+    w = W.WORKLOADS[name]
     per_set = bwd_bytes(w)
     R = max(1, min(4, math.ceil(2 * MALL_BYTES / per_set)))
     sets = []
@@ -276,11 +308,20 @@ def bench_bwd(args, torch, ssm, W):
                      checkpoints=x["ck"])
     msv = timed(n, False, saved=True)
     b = bwd_bytes(w)
-    return {"workload": w.name, "rotated_input_sets": R, "call_ms": mean, "call_ms_median": ms[n // 2],
-            "value": w.updates / (mean * 1e-3), "unit": "state-updates/s",
-            "workspace_bytes": need, "algorithmic_bytes_per_call": b,
-            "hbm_GBs": b / (mean * 1e-3) / 1e9, "zoh_call_ms": sum(mz) / len(mz),
-            "from_saved_checkpoints_call_ms": sum(msv) / len(msv)}
+    flops = w.updates * BWD_FLOPS_PER_UPDATE / (mean * 1e-3) / 1e12
+    gbs = b / (mean * 1e-3) / 1e9
+    rec = {"workload": w.name, "rotated_input_sets": R, "call_ms": mean, "call_ms_median": ms[n // 2],
+           "value": w.updates / (mean * 1e-3), "unit": "state-updates/s", "workspace_bytes": need,
+           "roofline": {"bound": "alu", "achieved": flops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": flops / FP32_PEAK_TFLOPS, "flops_per_update": BWD_FLOPS_PER_UPDATE,
+                        "traffic": traffic_from_profile("bwd_" + w.name, 1), "call_ms": mean},
+           "hbm": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                   "algorithmic_bytes_per_call": b},
+           "zoh_call_ms": sum(mz) / len(mz), "from_saved_checkpoints_call_ms": sum(msv) / len(msv)}
+    log("backward %s: %.4f ms/call -> %.3e updates/s, %.2f TFLOP/s (from saved checkpoints %.4f ms, ZOH %.4f ms)"
+        % (w.name, mean, rec["value"], flops, rec["from_saved_checkpoints_call_ms"], rec["zoh_call_ms"]))
+    del sets, ws, grads
+    return rec
 
 
 def conv_bytes(w, K) -> int:
@@ -299,10 +340,10 @@ def conv_step_bytes(w, K) -> int:
     return 2 * s * BD * (K - 1) + 2 * s * BD + 4 * w.dim * (K + 1)
 
 
-def bench_conv(args, torch, ssm, W, K=4):
-    """The conv + SiLU step that produces u, on the scan workload's [B, D, L] shape, and its
+def bench_conv(args, torch, ssm, W, K=4, name="mamba130m"):
+    """The conv + SiLU step that produces u, on a layer workload's [B, D, L] shape, and its
     decode form on the generation workload; events bracket each launch on the launch stream."""
-    w = W.WORKLOADS[args.workload]
+    w = W.WORKLOADS[name]
     per_set = conv_bytes(w, K)
     R = max(1, min(8, math.ceil(2 * MALL_BYTES / per_set)))
     sets = []
@@ -409,47 +450,102 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(torch, x, w, seconds):
-    """The fp64 oracle as it stands, on this host's cores, over the same inputs (repeated to ~seconds)."""
+def cpu_baseline(torch, x, w, seconds, rows=128):
+    """The fp64 oracle as it stands, on this host's cores (its OpenMP default), over a bounded
+    sample of the same inputs: the first `rows` channels of batch row 0 over the whole sequence
+    (repeated to ~seconds); also one thread on 4 channels."""
     sys.path.insert(0, ROOT)
     import numpy as np
     import oracle
 
-    host = {k: (None if v is None else np.ascontiguousarray(v.detach().to("cpu", torch.float64).numpy()))
-            for k, v in x.items() if k not in ("out", "fs")}
-    B_rows = w.batch
-    upd = 0
-    t0 = time.perf_counter()
-    runs = 0
-    while True:
-        oracle.scan(host["u"], host["delta"], host["A"], host["B"], host["C"], D=host["D"], z=host["z"],
-                    delta_bias=host["delta_bias"])
-        upd += w.batch * w.dim * w.dstate * w.seqlen
-        runs += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    cores = oracle.max_threads()
-    t1 = time.perf_counter()
-    oracle.scan(host["u"], host["delta"], host["A"], host["B"], host["C"], D=host["D"], z=host["z"],
-                delta_bias=host["delta_bias"], threads=1)
-    one = w.batch * w.dim * w.dstate * w.seqlen / (time.perf_counter() - t1)
-    return {"value": upd / dt, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+    rows = min(rows, w.dim)
+
+    def take(t, nrow):
+        if t is None:
+            return None
+        if t.dim() == 3 and t.shape[1] == w.dim and t.shape[2] == w.seqlen:  # [B, D, L] streams
+            t = t[:1, :nrow]
+        elif t.dim() == 3:  # B, C [B, N, L]
+            t = t[:1]
+        elif t.dim() == 2:  # A [D, N]
+            t = t[:nrow]
+        else:  # D, bias [D]
+            t = t[:nrow]
+        return np.ascontiguousarray(t.detach().to("cpu", torch.float64).numpy())
+
+    def run(nrow, threads, budget):
+        h = {k: take(v, nrow) for k, v in x.items() if k not in ("out", "fs")}
+        upd, runs = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.scan(h["u"], h["delta"], h["A"], h["B"], h["C"], D=h["D"], z=h["z"],
+                        delta_bias=h["delta_bias"], threads=threads)
+            upd += nrow * w.dstate * w.seqlen
+            runs += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return upd / (time.perf_counter() - t0), runs, time.perf_counter() - t0
+
+    v, runs, dt = run(rows, 0, seconds)
+    one, _, _ = run(4, 1, 0.0)
+    return {"value": v, "unit": "state-updates/s", "cores": oracle.max_threads(), "kind": "oracle",
             "cpu_model": cpu_model(), "value_1_thread": one,
-            "sample": "%d full pass(es) of the %s workload (%d x %d x %d x %d, the same bf16 inputs widened "
-                      "to fp64), %.1f s wall" % (runs, w.name, B_rows, w.dim, w.dstate, w.seqlen, dt)}
+            "sample": "%d pass(es) over the first %d channels of the %s workload (1 x %d x %d x %d: all %d steps, "
+                      "the same bf16 inputs widened to fp64), %.1f s wall; one thread: 4 channels"
+                      % (runs, rows, w.name, rows, w.dstate, w.seqlen, w.seqlen, dt)}
+
+
+def issue_probe():
+    """Measured issue rate of plain wave64 fp32 VALU work (v_fma_f32) and of v_exp_f32, 8 waves per
+    SIMD, from the probe library built beside the scan library (None if it is not built)."""
+    path = os.path.join(ROOT, "selective_state_space_76_amd", "libssmprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.ssm_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.ssm_probe_issue.restype = ctypes.c_int
+    res = {}
+    for kind, name in ((0, "v_fma_f32"), (1, "v_exp_f32")):
+        clk, ms = ctypes.c_double(), ctypes.c_double()
+        rc = lib.ssm_probe_issue(kind, 8, 2000, 2.4, ctypes.byref(clk), ctypes.byref(ms))
+        if rc != 0:
+            return None
+        res[name] = clk.value
+    lanes = 1024 * 64 * 2.4e9  # SIMDs x lanes x clock
+    fma_rate = lanes / res["v_fma_f32"]
+    return {"clk_per_wave64_instr_at_2p4GHz": res, "waves_per_simd": 8,
+            "fma_tflops_unpacked": 2 * fma_rate / 1e12,
+            "exp_per_s": lanes / res["v_exp_f32"],
+            "note": "one wave64 v_fma_f32 per ~4 clk per SIMD: 16 fp32 lanes per clock, half the published peak, "
+                    "which counts packed two-per-lane FMAs; this library is built without packed fp32"}
+
+
+def input_digest(torch, x):
+    """fp64 sums of every input and a 64-bit hash of its first 16 MiB (its bytes as stored)."""
+    sums, hashes = {}, {}
+    for k, v in x.items():
+        if v is None or k in ("out", "fs"):
+            continue
+        sums[k] = float(v.double().sum())
+        raw = v.contiguous().view(-1).view(torch.uint8)[: 16 << 20]
+        hashes[k] = hashlib.blake2b(raw.cpu().numpy().tobytes(), digest_size=8).hexdigest()
+    return sums, hashes
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mamba130m", choices=["mamba130m", "mamba1p3b", "dna1m", "tiny"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dna1m", choices=["dna1m", "mamba130m", "mamba1p3b", "tiny"],
+                    help="headline scan workload (default: the largest, dna1m)")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-configs", action="store_true", help="skip the layer-shape scan sub-records")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -479,53 +575,55 @@ def main():
     from selective_state_space_76_amd import workloads as W
     ssm.load()
 
-    w, R, ms_step, launch_ms, all_launch, x0, flushed = bench_scan(args, torch, ssm, W)
-    upd = w.updates
-    b = scan_bytes(w)
-    value = upd / (ms_step * 1e-3)
-    alu = upd * OPS_PER_UPDATE / (launch_ms * 1e-3) / 1e12
-    gbs = b / (launch_ms * 1e-3) / 1e9
-    log("scan: %.4f ms/step (wall), %.4f ms/launch (events) -> %.3e updates/s, %.1f GB/s"
-        % (ms_step, launch_ms, value, gbs))
+    head, w, x0 = scan_record(args, torch, ssm, W, args.workload, args.steps, args.warmup, keep_inputs=True)
+    sums, hashes = input_digest(torch, x0)
+    io = ssm.SSM_BF16 if w.io == "bf16" else ssm.SSM_F32
     res = {
-        "metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["value"], "unit": "state-updates/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen,
-                   "io_dtype": w.io, "state_dtype": "f32", "rotated_input_sets": R},
-        "roofline": {"bound": "alu", "achieved": alu, "peak": ALU_PEAK_TOPS, "unit": "T fp32-op/s",
-                     "frac": alu / ALU_PEAK_TOPS, "traffic": traffic_from_profile(w.name, 1),
-                     "ops_per_update": OPS_PER_UPDATE, "launch_ms": launch_ms,
-                     "launch_ms_median": all_launch[len(all_launch) // 2],
-                     "launch_ms_p10": all_launch[len(all_launch) // 10],
-                     "launch_ms_p90": all_launch[(9 * len(all_launch)) // 10],
-                     "flushed_launch_ms_median": flushed[len(flushed) // 2],
-                     "flushed_launch_ms_p10": flushed[len(flushed) // 10],
-                     "flushed_launch_ms_p90": flushed[(9 * len(flushed)) // 10]},
-        "hbm": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "algorithmic_bytes_per_launch": b},
+                   "io_dtype": w.io, "state_dtype": "f32", "rotated_input_sets": head["rotated_input_sets"],
+                   "workspace_bytes": ssm.workspace_size(w.batch, w.dim, w.dstate, w.seqlen, io)},
+        "roofline": head["roofline"],
+        "hbm": head["hbm"],
+        "call_ms": head["call_ms"], "call_ms_median": head["call_ms_median"],
+        "call_ms_p10": head["call_ms_p10"], "call_ms_p90": head["call_ms_p90"],
         "kernel_source_hash": kernel_source_hash(),
-        "input_fp64_sums": {k: float(v.double().sum()) for k, v in x0.items()
-                            if v is not None and k not in ("out", "fs")},
-        "input_hash64": {k: hashlib.blake2b(v.contiguous().view(torch.uint8).cpu().numpy().tobytes(),
-                                            digest_size=8).hexdigest()
-                         for k, v in x0.items() if v is not None and k not in ("out", "fs")},
+        "input_fp64_sums": sums, "input_hash64_first16MiB": hashes,
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(torch, x0, w, args.cpu_seconds)
+        log("cpu baseline: %.3e updates/s on %d threads (%s)" % (res["cpu_baseline"]["value"],
+                                                                  res["cpu_baseline"]["cores"],
+                                                                  res["cpu_baseline"]["sample"]))
+    del x0
+    torch.cuda.empty_cache()
     cp = copy_peak(torch)
     res["hbm"]["copy_peak_GBs"] = cp
-    res["hbm"]["frac_of_copy_peak"] = gbs / cp
+    res["hbm"]["frac_of_copy_peak"] = res["hbm"]["achieved"] / cp
     log("device copy (torch copy_, 1 GiB): %.1f GB/s" % cp)
+    if not args.no_configs:
+        res["configs"] = {}
+        for name in SUB_CONFIGS:
+            if name == w.name:
+                continue
+            rec, _, _ = scan_record(args, torch, ssm, W, name, max(args.steps, 20), max(args.warmup, 3))
+            rec["hbm"]["frac_of_copy_peak"] = rec["hbm"]["achieved"] / cp
+            res["configs"][name] = rec
+            torch.cuda.empty_cache()
     if not args.no_decode:
         d = bench_decode(args, torch, ssm, W)
         log("decode: %.4f ms/step eager wall, %.4f ms/step eager events, %.4f ms/step graph, %.1f GB/s"
             % (d["eager_wall_ms_per_step"], d["eager_gpu_ms_per_step"], d["gpu_ms_per_step"], d["roofline"]["achieved"]))
         res["decode"] = d
         d["roofline"]["frac_of_copy_peak"] = d["roofline"]["achieved"] / cp
+        torch.cuda.empty_cache()
     if not args.no_bwd:
-        bw = bench_bwd(args, torch, ssm, W)
-        log("backward: %.4f ms/call -> %.3e updates/s (from saved checkpoints %.4f ms, ZOH %.4f ms)"
-            % (bw["call_ms"], bw["value"], bw["from_saved_checkpoints_call_ms"], bw["zoh_call_ms"]))
-        res["backward"] = bw
+        res["backward"] = {}
+        for name in SUB_CONFIGS:
+            res["backward"][name] = bench_bwd(args, torch, ssm, W, name)
+            torch.cuda.empty_cache()
     if not args.no_conv:
         pre, dec = bench_conv(args, torch, ssm, W)
         log("conv1d: %.4f ms/launch, %.1f GB/s; conv1d_update: %.4f ms/step, %.1f GB/s"
@@ -534,9 +632,11 @@ def main():
         dec["roofline"]["frac_of_copy_peak"] = dec["roofline"]["achieved"] / cp
         res["conv1d"] = pre
         res["conv1d_update"] = dec
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(torch, x0, w, args.cpu_seconds)
-        log("cpu baseline: %.3e updates/s on %d threads" % (res["cpu_baseline"]["value"], res["cpu_baseline"]["cores"]))
+    if not args.no_probe:
+        pr = issue_probe()
+        if pr is not None:
+            res["alu_issue_probe"] = pr
+            log("issue probe: %s clk per wave64 instruction per SIMD" % pr["clk_per_wave64_instr_at_2p4GHz"])
     print(json.dumps(res), flush=True)
 
 

@@ -41,6 +41,23 @@ def _compile_cmd(src: str, obj: str):
     return [hipcc()] + HIPCC_FLAGS + ["-c", src, "-o", obj]
 
 
+PROBE_SRC = os.path.join(CSRC, "issue_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libssmprobe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The VALU issue-rate probe bench.py reports beside the scan (a separate library, not the ABI)."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), r.stdout))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every HIP/C++ source of the library (in parallel) and link libssmscan.so."""
     from concurrent.futures import ThreadPoolExecutor
@@ -73,3 +90,4 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
