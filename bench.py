@@ -496,8 +496,9 @@ def cpu_baseline(torch, x, w, seconds, rows=128):
 
 
 def issue_probe():
-    """Measured issue rate of plain wave64 fp32 VALU work (v_fma_f32) and of v_exp_f32, 8 waves per
-    SIMD, from the probe library built beside the scan library (None if it is not built)."""
+    """Measured issue rates, 8 waves per SIMD, from the probe library built beside the scan library
+    (None if it is not built): plain wave64 fp32 work (v_fma_f32), v_exp_f32, and a multiply with a
+    DPP row-broadcast operand."""
     path = os.path.join(ROOT, "selective_state_space_76_amd", "libssmprobe.so")
     if not os.path.exists(path):
         return None
@@ -506,19 +507,16 @@ def issue_probe():
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.ssm_probe_issue.restype = ctypes.c_int
     res = {}
-    for kind, name in ((0, "v_fma_f32"), (1, "v_exp_f32")):
+    for kind, name in ((0, "v_fma_f32"), (1, "v_exp_f32"), (2, "v_mul_f32_dpp_row_bcast")):
         clk, ms = ctypes.c_double(), ctypes.c_double()
-        rc = lib.ssm_probe_issue(kind, 8, 2000, 2.4, ctypes.byref(clk), ctypes.byref(ms))
-        if rc != 0:
+        if lib.ssm_probe_issue(kind, 8, 1000, 2.4, ctypes.byref(clk), ctypes.byref(ms)) != 0:
             return None
         res[name] = clk.value
     lanes = 1024 * 64 * 2.4e9  # SIMDs x lanes x clock
-    fma_rate = lanes / res["v_fma_f32"]
     return {"clk_per_wave64_instr_at_2p4GHz": res, "waves_per_simd": 8,
-            "fma_tflops_unpacked": 2 * fma_rate / 1e12,
-            "exp_per_s": lanes / res["v_exp_f32"],
-            "note": "one wave64 v_fma_f32 per ~4 clk per SIMD: 16 fp32 lanes per clock, half the published peak, "
-                    "which counts packed two-per-lane FMAs; this library is built without packed fp32"}
+            "fma_tflops": 2 * lanes / res["v_fma_f32"] / 1e12, "exp_per_s": lanes / res["v_exp_f32"],
+            "note": "fp32 FMA issue rate of the whole GPU, unpacked (against the published 157.3 TFLOP/s); "
+                    "v_exp_f32 and DPP-sourced operations issue at a fraction of it"}
 
 
 def input_digest(torch, x):

@@ -1,51 +1,60 @@
 // issue_probe.hip -- measurement helper for bench.py (not part of the scan library's ABI).
 //
 // Times long runs of one kind of wave64 fp32 VALU instruction on every SIMD of the GPU, so the
-// benchmark can state what issue rate the scan's instruction mix is held to: the published fp32
-// vector peak counts packed (two-per-lane) FMAs, which this library's kernels are built without.
-// Each lane runs 8 independent chains (no dependency stalls); one workgroup of 4 waves per CU and
-// per requested wave per SIMD.
+// benchmark can state the issue rates the scan's instruction mix is held to: plain VALU work
+// (v_fma_f32), the transcendental v_exp_f32, and a multiply whose operand comes through a DPP row
+// broadcast.  The loop is written in assembly with fixed registers: 8 independent chains in
+// registers of VGPR banks 2 and 3, the shared operands in banks 0 and 1, so no instruction reads
+// two operands from one bank (which costs extra cycles).  One workgroup of 4 waves per CU per
+// requested wave per SIMD.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace {
 
-#define PROBE_X8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
+#define PROBE_REP8(X) X X X X X X X X
+#define PROBE_FMA8                                                                                         \
+  "v_fma_f32 v42, v42, v48, v49\n v_fma_f32 v43, v43, v48, v49\n v_fma_f32 v46, v46, v48, v49\n"           \
+  "v_fma_f32 v47, v47, v48, v49\n v_fma_f32 v50, v50, v48, v49\n v_fma_f32 v51, v51, v48, v49\n"           \
+  "v_fma_f32 v54, v54, v48, v49\n v_fma_f32 v55, v55, v48, v49\n"
+#define PROBE_EXP8                                                                                         \
+  "v_exp_f32 v42, -|v42|\n v_exp_f32 v43, -|v43|\n v_exp_f32 v46, -|v46|\n v_exp_f32 v47, -|v47|\n"       \
+  "v_exp_f32 v50, -|v50|\n v_exp_f32 v51, -|v51|\n v_exp_f32 v54, -|v54|\n v_exp_f32 v55, -|v55|\n"
+#define PROBE_DPP(r) "v_mul_f32_dpp " r ", " r ", v48 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+#define PROBE_DPP8                                                                                         \
+  PROBE_DPP("v42") PROBE_DPP("v43") PROBE_DPP("v46") PROBE_DPP("v47") PROBE_DPP("v50") PROBE_DPP("v51")   \
+  PROBE_DPP("v54") PROBE_DPP("v55")
+#define PROBE_INIT                                                                                         \
+  "v_mov_b32 v42, 0.5\n v_mov_b32 v43, 0.5\n v_mov_b32 v46, 0.5\n v_mov_b32 v47, 0.5\n"                   \
+  "v_mov_b32 v50, 0.5\n v_mov_b32 v51, 0.5\n v_mov_b32 v54, 0.5\n v_mov_b32 v55, 0.5\n"                   \
+  "v_mov_b32 v48, 0.999\n v_mov_b32 v49, 0.001\n s_mov_b32 s20, %1\n s_nop 1\n"
+#define PROBE_LOOP(BODY)                                                                                   \
+  asm volatile(PROBE_INIT "1:\n" BODY "s_sub_u32 s20, s20, 1\n s_cmp_lg_u32 s20, 0\n s_cbranch_scc1 1b\n"  \
+               "v_add_f32 %0, v42, v55\n"                                                                  \
+               : "=v"(r)                                                                                   \
+               : "s"(iters)                                                                                \
+               : "v42", "v43", "v46", "v47", "v48", "v49", "v50", "v51", "v54", "v55", "s20", "scc")
 
 template <int KIND>
 __global__ __launch_bounds__(256) void probe_kernel(float* out, int iters) {
-  float a0 = 0.5f + threadIdx.x * 1e-3f, a1 = a0 + 0.1f, a2 = a0 + 0.2f, a3 = a0 + 0.3f;
-  float a4 = a0 + 0.4f, a5 = a0 + 0.5f, a6 = a0 + 0.6f, a7 = a0 + 0.7f;
-  const float m = 0.999f, c = 0.001f;
-  for (int i = 0; i < iters; ++i) {
-    if constexpr (KIND == 0) {  // 64 x v_fma_f32
-#define PROBE_F(j) "v_fma_f32 %" #j ", %" #j ", %8, %9\n"
-      asm volatile(PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F)
-                   PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F)
-                   : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7)
-                   : "v"(m), "v"(c));
-#undef PROBE_F
-    } else {  // 64 x v_exp_f32 (argument kept in (-inf, 0] so values stay bounded)
-#define PROBE_F(j) "v_exp_f32 %" #j ", -|%" #j "|\n"
-      asm volatile(PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F)
-                   PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F) PROBE_X8(PROBE_F)
-                   : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
-#undef PROBE_F
-    }
-  }
-  out[(size_t)blockIdx.x * 256 + threadIdx.x] = a0 + a1 + a2 + a3 + a4 + a5 + a6 + a7;
+  float r = 0.0f;
+  if constexpr (KIND == 0) PROBE_LOOP(PROBE_REP8(PROBE_FMA8));
+  if constexpr (KIND == 1) PROBE_LOOP(PROBE_REP8(PROBE_EXP8));
+  if constexpr (KIND == 2) PROBE_LOOP(PROBE_REP8(PROBE_DPP8));
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
 }
 
 }  // namespace
 
 extern "C" {
 
-// kind 0: v_fma_f32, 1: v_exp_f32.  waves_per_simd in [1, 8].  On success returns 0 and writes
-// the SIMD cycles per wave64 instruction at clock_ghz (event time x clock / instructions per SIMD)
-// and the elapsed milliseconds; -1 on bad arguments, -2 on a HIP error.
+// kind 0: v_fma_f32, 1: v_exp_f32, 2: v_mul_f32 with a DPP row-broadcast operand; 64 instructions
+// per loop iteration.  waves_per_simd in [1, 8].  On success returns 0 and writes the SIMD cycles per
+// wave64 instruction at clock_ghz (event time x clock / instructions per SIMD) and the elapsed
+// milliseconds; -1 on bad arguments, -2 on a HIP error.
 int ssm_probe_issue(int kind, int waves_per_simd, int iters, double clock_ghz, double* clk_per_instr,
                     double* ms_out) {
-  if ((kind != 0 && kind != 1) || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 || !clk_per_instr)
+  if (kind < 0 || kind > 2 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 || !clk_per_instr)
     return -1;
   int dev = 0;
   hipDeviceProp_t prop;
@@ -60,7 +69,8 @@ int ssm_probe_issue(int kind, int waves_per_simd, int iters, double clock_ghz, d
   for (int rep = 0; rep < 3 && err == hipSuccess; ++rep) {  // the last repetition is timed
     err = hipEventRecord(e0, nullptr);
     if (kind == 0) hipLaunchKernelGGL(probe_kernel<0>, dim3(blocks), dim3(256), 0, nullptr, out, iters);
-    else hipLaunchKernelGGL(probe_kernel<1>, dim3(blocks), dim3(256), 0, nullptr, out, iters);
+    else if (kind == 1) hipLaunchKernelGGL(probe_kernel<1>, dim3(blocks), dim3(256), 0, nullptr, out, iters);
+    else hipLaunchKernelGGL(probe_kernel<2>, dim3(blocks), dim3(256), 0, nullptr, out, iters);
     if (err == hipSuccess) err = hipGetLastError();
     if (err == hipSuccess) err = hipEventRecord(e1, nullptr);
     if (err == hipSuccess) err = hipEventSynchronize(e1);

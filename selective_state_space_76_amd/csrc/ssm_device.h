@@ -279,8 +279,19 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
     }
   }
 
+  // Blocks wholly inside the rows (16-byte rows): unconditional loads from addresses that are valid
+  // for every chunk slot (slots that are not live are never stored, so what they load is unused).
+  const IO* fsrc[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+    fsrc[k] = (src[k] ? src[k] : reinterpret_cast<const IO*>(p.u)) + (REV ? (L - EPC - col[k]) : col[k]);
   uint4 raw[CPT];
   auto fetch = [&](int64_t t0) {
+    if (VEC && t0 + 64 <= L) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) raw[k] = *reinterpret_cast<const uint4*>(fsrc[k] + (REV ? -t0 : t0));
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int64_t ts = t0 + col[k];  // first logical step of the chunk
@@ -454,6 +465,45 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
           ys[2] = s == 2 ? yv : ys[2];
           ys[3] = s == 3 ? yv : ys[3];
         }
+      }
+    } else if constexpr (NL > 1) {
+      // Several states per lane: per sub-block the 16 step values are broadcast once, then each state
+      // slice reads its own B/C and runs its decay factors, chain and C.h terms before the next slice
+      // starts (fewer live registers than all slices' factors at once).
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float dj[16], xj[16], pj[16];
+        static_for<0, 16>([&](auto j_) {
+          constexpr int j = decltype(j_)::value;
+          dj[j] = row_bcast<j>(dl[s]);
+          xj[j] = row_bcast<j>(xu[s]);
+        });
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          float hi = h[i];
+          // an empty asm that makes this slice's chain start after the previous slice's C.h terms
+          if (i > 0) asm volatile("" : "+v"(hi) : "v"(MODE == 0 ? pj[15] : h[i > 0 ? i - 1 : 0]) : "memory");
+          float bb[16], cc[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 vb = *reinterpret_cast<const float4*>(Bt + (g + 16 * i) * TS + 16 * s + 4 * q);
+            bb[4 * q] = vb.x; bb[4 * q + 1] = vb.y; bb[4 * q + 2] = vb.z; bb[4 * q + 3] = vb.w;
+            if (MODE == 0) {
+              const float4 vc = *reinterpret_cast<const float4*>(Ct + (g + 16 * i) * TS + 16 * s + 4 * q);
+              cc[4 * q] = vc.x; cc[4 * q + 1] = vc.y; cc[4 * q + 2] = vc.z; cc[4 * q + 3] = vc.w;
+            }
+          }
+          float av[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) av[j] = exp2_(dj[j] * Ap[i]);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            hi = __builtin_fmaf(av[j], hi, xj[j] * bb[j]);
+            if (MODE == 0) pj[j] = (i == 0) ? cc[j] * hi : __builtin_fmaf(cc[j], hi, pj[j]);
+          }
+          h[i] = hi;
+        }
+        if (MODE == 0) ys[s] = (row_transpose_sum(pj) + Dd * uu[s]) * gz[s];
       }
     } else {
 #pragma unroll

@@ -20,6 +20,49 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(g - r) / den)) if r.size else 0.0
 
 
+def bf16_rne(x):
+    """float64 values rounded to the nearest bfloat16 (ties to even), exactly; returned as float64."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def bf16_ulps(got, ref):
+    """Distance in bf16 ulps between bf16 results and the exact values rounded to bf16."""
+    g = got.detach().to("cpu").contiguous().view(torch.int16).numpy().astype(np.int32)
+    r = torch.from_numpy(bf16_rne(ref).astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    r = r.numpy().astype(np.int32)
+
+    def order(b):  # sign-magnitude bit patterns to a monotone integer scale
+        return np.where(b < 0, -(b & 0x7FFF), b)
+    return np.abs(order(g) - order(r))
+
+
+ULP_FLOOR = 2.0 ** -12  # elements below this fraction of rms(ref) are held to an absolute bound
+ULP_SMALL_ABS = 2.0 ** -16  # that bound, as a fraction of rms(ref)
+
+
+def check_bf16_ulp(got, ref, what=""):
+    """bf16 results within one bf16 ulp of the fp64 result rounded to bf16 (RNE).  A result is
+    rounded once from fp32, so this holds wherever the fp32 arithmetic before the rounding errs by
+    less than an ulp; that fails only for elements far below the tensor's scale, where fp32
+    cancellation (in the sum over states, an adjoint term) can exceed an ulp of the element itself.
+    Elements smaller than ULP_FLOOR * rms(ref) are therefore held to |got - ref| <= ULP_SMALL_ABS *
+    rms(ref) instead.  fp32 results are not checked here."""
+    if got.dtype != torch.bfloat16:
+        return
+    r = np.asarray(ref, np.float64).reshape(tuple(got.shape))
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    big = np.abs(r) >= ULP_FLOOR * rms
+    d = bf16_ulps(got, r)
+    worst = int(d[big].max()) if big.any() else 0
+    g = got.detach().to("cpu", torch.float64).numpy()
+    small = float(np.max(np.abs(g[~big] - r[~big]))) / max(rms, 1e-300) if (~big).any() else 0.0
+    print("%s bf16 ulps: max %d over %d elements (%d at 1 ulp); %d small elements, max err %.2g rms"
+          % (what, worst, int(big.sum()), int((d[big] == 1).sum()), int((~big).sum()), small), flush=True)
+    assert worst <= 1, (what, worst)
+    assert small <= ULP_SMALL_ABS, (what, small)
+
+
 def tol_for(x: torch.Tensor) -> float:
     return TOL_F32 if x.dtype == torch.float32 else TOL_BF16
 

@@ -15,7 +15,7 @@ import torch
 import oracle
 from selective_state_space_76_amd import SSM_F32, bwd_workspace_size, checkpoints_shape, scan_bwd, scan_fwd
 from selective_state_space_76_amd import workloads as W
-from tests.gpu_util import rel_err, tol_for
+from tests.gpu_util import check_bf16_ulp, rel_err, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,9 @@ def check(x, reverse=False, tol=None, zoh=False):
     print("rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()), flush=True)
     bad = {k: e for k, e in errs.items() if not e <= tol}
     assert not bad, bad
+    for k in ("du", "ddelta", "dz"):  # the gradients returned in the stream dtype
+        if g[k] is not None and ref[k] is not None:
+            check_bf16_ulp(g[k], ref[k], k)
     return g
 
 
@@ -189,6 +192,9 @@ def _sampled_channel_check(w, chans, dout_seed):
     print("sampled rel_err " + " ".join("%s=%.2g" % kv for kv in errs.items()), flush=True)
     bad = {k: e for k, e in errs.items() if not e <= tol_for(x["u"])}
     assert not bad, bad
+    for k in ("du", "ddelta", "dz"):
+        if got[k] is not None and ref[k] is not None:
+            check_bf16_ulp(got[k], ref[k], k)
 
 
 def test_bwd_workload_mamba1p3b_sampled():

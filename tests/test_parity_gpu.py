@@ -11,7 +11,7 @@ import torch
 import oracle
 from selective_state_space_76_amd import scan_fwd, state_update, workspace_size
 from selective_state_space_76_amd import workloads as W
-from tests.gpu_util import oracle_rows, rel_err, sample_rows, tol_for
+from tests.gpu_util import check_bf16_ulp, oracle_rows, rel_err, sample_rows, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,7 @@ def full_check(inp, h0=None, zoh=False, reverse=False, split=True, tol=None):
     ey, eh = rel_err(out, ref_y), rel_err(fs, ref_h)
     print("rel_err y=%.3g state=%.3g tol=%g" % (ey, eh, tol), flush=True)
     assert ey <= tol and eh <= tol, (ey, eh)
+    check_bf16_ulp(out, ref_y, "y")
     return out, fs
 
 
@@ -113,6 +114,7 @@ def test_full_workload_sampled(name):
     ey, eh = rel_err(got_y, ref_y), rel_err(got_h, ref_h)
     print("%s rel_err y=%.3g state=%.3g" % (name, ey, eh), flush=True)
     assert ey <= 2e-2 and eh <= 2e-2
+    check_bf16_ulp(got_y, ref_y, name + " y")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
@@ -133,6 +135,7 @@ def test_state_update_small(dtype, N):
         tol = 1e-4 if dtype == torch.float32 else 2e-2
         ey, es = rel_err(y, ref_y), rel_err(st, state)
         assert ey <= tol and es <= tol, (k, ey, es)
+        check_bf16_ulp(y, ref_y, "step %d y" % k)
 
 
 def test_decode_workload_sampled():
@@ -157,6 +160,7 @@ def test_decode_workload_sampled():
         if k % 100 == 99 or k == 0:
             worst = max(worst, rel_err(sub(y), ref_y), rel_err(sub(st), ref_state))
             print("step %d worst rel_err %.3g" % (k, worst), flush=True)
+            check_bf16_ulp(sub(y), ref_y, "step %d y" % k)
     assert worst <= 2e-2
 
 
