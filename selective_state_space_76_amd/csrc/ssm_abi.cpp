@@ -15,6 +15,7 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 40;
 constexpr int64_t kMaxElems = int64_t(1) << 61;
 constexpr int kTargetBlocks = 1024;    // 4 workgroups of 4 waves per CU on 256 CUs
+constexpr int kTargetBlocksCl = 1024;  // 4 output-pass workgroups per CU on 256 CUs (channels on lanes)
 constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
 
 struct Range {
@@ -39,6 +40,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 struct Plan {
   int64_t S = 1, seg_len = 0, nblk = 0;
+  bool cl = false;  // the split runs with channels on lanes (scan_cl.hip)
   size_t ws_state = 0, ws_dsum = 0, ws_carry = 0, total = 0;
 };
 
@@ -61,7 +63,15 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
   pl->S = 1;
   pl->seg_len = ((L + 63) / 64) * 64;
   if (base < kTargetBlocks / 2 && L >= 2 * kMinSegment) {
-    const int64_t want = (kTargetBlocks + base - 1) / base;
+    // bf16 streams, the default discretisation, up to 16 states and rows of whole 16-byte chunks:
+    // the split's passes keep channels on lanes, 64 channels per workgroup, and the segments
+    // supply the parallelism (when whole 64-channel groups pad D by at most a fifth)
+    const int64_t pad = (s->dim + 63) / 64 * 64 - s->dim;
+    pl->cl = s->io_dtype == SSM_BF16 && !(s->flags & SSM_FLAG_ZOH) && s->dstate <= 16 && L % 8 == 0 &&
+             L < (int64_t(1) << 24) && 5 * pad <= s->dim;
+    const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;
+    const int64_t target = pl->cl ? kTargetBlocksCl : kTargetBlocks;
+    const int64_t want = (target + units - 1) / units;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 63) / 64) * 64;
     if (seg < kMinSegment) seg = kMinSegment;
@@ -69,6 +79,8 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
     if (S > 1) {
       pl->S = S;
       pl->seg_len = seg;
+    } else {
+      pl->cl = false;
     }
   }
   if (base * pl->S > (int64_t(1) << 31) - 1) return false;
@@ -248,12 +260,14 @@ ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delt
   p.seg_state = reinterpret_cast<float*>(ws);
   p.seg_dsum = reinterpret_cast<float*>(ws + pl.ws_state);
   float* carries = reinterpret_cast<float*>(ws + pl.ws_state + pl.ws_dsum);
-  ssm_status rc = launch_status(ssm::launch_scan(p, bf16, 1, st));
+  // channels on lanes unless block checkpoints are wanted (the lanes-over-states kernels write them)
+  const bool cl = pl.cl && ckpt == nullptr;
+  ssm_status rc = launch_status(cl ? ssm::launch_scan_cl(p, 1, st) : ssm::launch_scan(p, bf16, 1, st));
   if (rc != SSM_OK) return rc;
   p.carries = carries;
   rc = launch_status(ssm::launch_carry(p, st));
   if (rc != SSM_OK) return rc;
-  return launch_status(ssm::launch_scan(p, bf16, 0, st));
+  return launch_status(cl ? ssm::launch_scan_cl(p, 0, st) : ssm::launch_scan(p, bf16, 0, st));
 }
 
 }  // namespace

@@ -90,6 +90,10 @@ struct ConvParams {
 };
 
 hipError_t launch_scan(const ScanParams& p, bool bf16, int mode, hipStream_t s);
+// the split's summary (mode 1) and output (mode 0) passes with channels on lanes: bf16 streams,
+// the default discretisation, N <= 16, L a multiple of 8 and below 2^24 (workgroups of 64
+// channels, ceil(Dm / 64) per batch row and segment)
+hipError_t launch_scan_cl(const ScanParams& p, int mode, hipStream_t s);
 // mode 0: per-element prefill, 1: 16-byte-chunk prefill (L a multiple of the chunk), 2: decode step
 hipError_t launch_conv(const ConvParams& p, bool bf16, int mode, hipStream_t s);
 hipError_t launch_carry(const ScanParams& p, hipStream_t s);

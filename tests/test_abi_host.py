@@ -107,11 +107,36 @@ def test_workspace_rules():
 def test_workspace_size_formula():
     # split planning: shape-only; segments of >= 1024 steps (multiples of 64) for narrow problems
     lib = L.load()
-    s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
-    S = 16                       # 64 channel blocks -> 16 segments of 65536 steps
     bdn, bd = 1024 * 16, 1024
     r = lambda x: (x + 255) // 256 * 256
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn)
+    want = lambda S: r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn)
+    # lanes over states (fp32 streams, or ZOH): 64 channel blocks of 16 -> 16 segments of 65536 steps
+    s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, io_dtype=L.SSM_F32)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
+    s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, flags=L.SSM_FLAG_ZOH)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
+    # channels on lanes (bf16, default discretisation, N <= 16, L % 8 == 0, L < 2^24): 16 groups
+    # of 64 channels -> 64 segments of 16384 steps (1024 workgroups of the output pass)
+    s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
+    # D = 1000 pads 24 channels to whole groups (under a fifth): still channels on lanes; D = 100
+    # would pad 28 (over a fifth) and L not a multiple of 8 breaks the 16-byte rows: lanes over states
+    s = shp(batch=1, dim=1000, dstate=16, seqlen=1 << 20)
+    b1, b2 = 1000 * 16, 1000
+    S = 64  # 16 groups
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * b1) + r(4 * (S - 1) * b2) + r(4 * S * b1)
+    s = shp(batch=1, dim=100, dstate=16, seqlen=1 << 16)
+    S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 147 segments wanted, held to 1024 steps each
+    b1, b2 = 100 * 16, 100
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * b1) + r(4 * (S - 1) * b2) + r(4 * S * b1)
+    s = shp(batch=1, dim=1024, dstate=16, seqlen=(1 << 20) - 4)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
+    # 2^24 steps: 64 rows of a stream pass 2^31 bytes, lanes over states (4 blocks of 16 channels
+    # -> 256 segments of 65536 steps; channels on lanes would take 1024)
+    s = shp(batch=1, dim=64, dstate=16, seqlen=1 << 24)
+    b1, b2 = 64 * 16, 64
+    S = 256
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * b1) + r(4 * (S - 1) * b2) + r(4 * S * b1)
 
 
 def test_bwd_workspace_size_split():

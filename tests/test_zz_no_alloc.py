@@ -37,6 +37,8 @@ CASES = [
      {"reverse": True}),
     ("bf16 64 states split then unsplit", torch.bfloat16, (1, 32, 64, 5000), (2, 48, 64, 700), {}),
     ("bf16 ZOH split with h0 then smaller", torch.bfloat16, (1, 24, 16, 8192), (1, 8, 16, 2048), {"zoh": True}),
+    ("bf16 channels-on-lanes split then smaller, reverse", torch.bfloat16, (1, 128, 16, 8192), (2, 64, 16, 4096),
+     {"reverse": True}),
 ]
 
 
