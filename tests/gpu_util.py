@@ -37,30 +37,34 @@ def bf16_ulps(got, ref):
     return np.abs(order(g) - order(r))
 
 
-ULP_FLOOR = 2.0 ** -12  # elements below this fraction of rms(ref) are held to an absolute bound
-ULP_SMALL_ABS = 2.0 ** -16  # that bound, as a fraction of rms(ref)
+ULP_SMALL_ABS = 2.0 ** -16  # absolute allowance for fp32 cancellation, as a fraction of rms(ref)
 
 
 def check_bf16_ulp(got, ref, what=""):
-    """bf16 results within one bf16 ulp of the fp64 result rounded to bf16 (RNE).  A result is
-    rounded once from fp32, so this holds wherever the fp32 arithmetic before the rounding errs by
-    less than an ulp; that fails only for elements far below the tensor's scale, where fp32
-    cancellation (in the sum over states, an adjoint term) can exceed an ulp of the element itself.
-    Elements smaller than ULP_FLOOR * rms(ref) are therefore held to |got - ref| <= ULP_SMALL_ABS *
-    rms(ref) instead.  fp32 results are not checked here."""
+    """bf16 results within one bf16 ulp of the fp64 result rounded to bf16 (RNE), or within
+    ULP_SMALL_ABS * rms(ref) of the fp64 result.  A result is rounded once from fp32, so one ulp
+    holds wherever the fp32 arithmetic before the rounding errs by less than an ulp of the element.
+    An element much smaller than the terms it sums (the sum over states, an adjoint term) keeps
+    the fp32 error of those terms, of order eps32 times their size, which exceeds an ulp of the
+    element itself; the absolute allowance covers that.  For elements of at least 2^-8 rms(ref)
+    one ulp is already above the allowance, so there the test is one ulp.  fp32 results are not
+    checked here."""
     if got.dtype != torch.bfloat16:
         return
     r = np.asarray(ref, np.float64).reshape(tuple(got.shape))
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-    big = np.abs(r) >= ULP_FLOOR * rms
     d = bf16_ulps(got, r)
-    worst = int(d[big].max()) if big.any() else 0
     g = got.detach().to("cpu", torch.float64).numpy()
-    small = float(np.max(np.abs(g[~big] - r[~big]))) / max(rms, 1e-300) if (~big).any() else 0.0
-    print("%s bf16 ulps: max %d over %d elements (%d at 1 ulp); %d small elements, max err %.2g rms"
-          % (what, worst, int(big.sum()), int((d[big] == 1).sum()), int((~big).sum()), small), flush=True)
-    assert worst <= 1, (what, worst)
-    assert small <= ULP_SMALL_ABS, (what, small)
+    err = np.abs(g - r) / max(rms, 1e-300)
+    allowed = err <= ULP_SMALL_ABS
+    bad = (d > 1) & ~allowed
+    big = np.abs(r) >= 2.0 ** -8 * rms
+    worst = int(d[big].max()) if big.any() else 0
+    print("%s bf16 ulps: max %d over %d elements >= 2^-8 rms (%d at 1 ulp); %d smaller elements more than "
+          "1 ulp off, max err %.2g rms" % (what, worst, int(big.sum()), int((d[big] == 1).sum()),
+                                           int(((d > 1) & ~big).sum()), float(err[(d > 1) & ~big].max())
+                                           if ((d > 1) & ~big).any() else 0.0), flush=True)
+    assert not bad.any(), (what, int(d[bad].max()), float(err[bad].max()))
 
 
 def tol_for(x: torch.Tensor) -> float:
