@@ -41,7 +41,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 struct Plan {
   int64_t S = 1, seg_len = 0, nblk = 0;
   bool cl = false;  // the split runs with channels on lanes (scan_cl.hip)
-  size_t ws_state = 0, ws_dsum = 0, ws_carry = 0, total = 0;
+  size_t ws_dsum = 0, ws_carry = 0, total = 0;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -85,10 +85,11 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
   }
   if (base * pl->S > (int64_t(1) << 31) - 1) return false;
   if (pl->S > 1) {
-    pl->ws_state = round256(sizeof(float) * (size_t)(pl->S - 1) * (size_t)bdn);
-    pl->ws_dsum = round256(sizeof(float) * (size_t)(pl->S - 1) * (size_t)bd);
+    // carries [S,B,D,N] (the summary pass writes segment s's end state into slot s + 1, and the
+    // carry pass turns it in place into the state entering segment s + 1), then the step-size sums
     pl->ws_carry = round256(sizeof(float) * (size_t)pl->S * (size_t)bdn);
-    pl->total = pl->ws_state + pl->ws_dsum + pl->ws_carry;
+    pl->ws_dsum = round256(sizeof(float) * (size_t)(pl->S - 1) * (size_t)bd);
+    pl->total = pl->ws_carry + pl->ws_dsum;
   }
   return true;
 }
@@ -98,7 +99,7 @@ ssm_status launch_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_E
 struct BwdPlan {
   int64_t nblk = 0, nbk = 0, S = 1, seg_len = 0;
   size_t ckpt = 0, bc = 0, a = 0, d = 0;
-  size_t seg_state = 0, seg_dsum = 0, carries = 0, adj_q = 0, adj_dsum = 0, adj_in = 0, total = 0;
+  size_t seg_dsum = 0, carries = 0, adj_q = 0, adj_dsum = 0, adj_in = 0, total = 0;
 };
 
 constexpr int kBwdTargetBlocks = 768;  // 3 backward workgroups per CU on 256 CUs
@@ -138,8 +139,7 @@ bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl, bool saved = false) {
   pl->a = round256(sizeof(float) * (size_t)x);
   pl->d = round256(sizeof(float) * (size_t)(2 * pl->S * BD));
   if (pl->S > 1) {
-    if (!saved) {  // the checkpoints' own split: end states, step-size sums, carries
-      pl->seg_state = round256(sizeof(float) * (size_t)((pl->S - 1) * BDN));
+    if (!saved) {  // the checkpoints' own split: carries (segment end states in place), step-size sums
       pl->seg_dsum = round256(sizeof(float) * (size_t)((pl->S - 1) * BD));
       pl->carries = round256(sizeof(float) * (size_t)(pl->S * BDN));
     }
@@ -147,7 +147,7 @@ bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl, bool saved = false) {
     pl->adj_dsum = round256(sizeof(float) * (size_t)(pl->S * BD));
     pl->adj_in = pl->adj_q;
   }
-  pl->total = pl->ckpt + pl->bc + pl->a + pl->d + pl->seg_state + pl->seg_dsum + pl->carries + pl->adj_q +
+  pl->total = pl->ckpt + pl->bc + pl->a + pl->d + pl->seg_dsum + pl->carries + pl->adj_q +
               pl->adj_dsum + pl->adj_in;
   return true;
 }
@@ -170,7 +170,7 @@ const char* ssm_status_str(int status) {
     case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_workspace_size()";
     case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SSM_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
-    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (8 MiB)";
+    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (5 MiB)";
     default: return "unknown status";
   }
 }
@@ -257,9 +257,9 @@ ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delt
   char* ws = static_cast<char*>(workspace);
   p.S = (int)pl.S;
   p.seg_len = pl.seg_len;
-  p.seg_state = reinterpret_cast<float*>(ws);
-  p.seg_dsum = reinterpret_cast<float*>(ws + pl.ws_state);
-  float* carries = reinterpret_cast<float*>(ws + pl.ws_state + pl.ws_dsum);
+  float* carries = reinterpret_cast<float*>(ws);
+  p.seg_state = carries + Bsz * Dm * N;  // slots 1 .. S-1 of the carries, overwritten in place
+  p.seg_dsum = reinterpret_cast<float*>(ws + pl.ws_carry);
   // channels on lanes unless block checkpoints are wanted (the lanes-over-states kernels write them)
   const bool cl = pl.cl && ckpt == nullptr;
   ssm_status rc = launch_status(cl ? ssm::launch_scan_cl(p, 1, st) : ssm::launch_scan(p, bf16, 1, st));
@@ -405,9 +405,9 @@ ssm_status scan_bwd_impl(const ssm_shape* shape, const void* u, const void* delt
   float* part_bc = take(pl.bc);
   float* part_a = take(pl.a);
   float* part_d = take(pl.d);
-  float* seg_state = take(pl.seg_state);
   float* seg_dsum = take(pl.seg_dsum);
   float* carries = take(pl.carries);
+  float* seg_state = carries + Bsz * Dm * N;  // slots 1 .. S-1 of the carries, overwritten in place
   float* adj_q = take(pl.adj_q);
   float* adj_dsum = take(pl.adj_dsum);
   float* adj_in = take(pl.adj_in);

@@ -41,7 +41,9 @@ hipError_t scratch_buffer(hipStream_t stream, void** ptr) {
   return hipSuccess;
 }
 
-// Chains the segment summaries: carries[s] is the state entering segment s.
+// Chains the segment summaries: carries[s] is the state entering segment s.  seg_state may lie in
+// the carries' own slots 1 .. S-1 (segment s's end state where the state entering segment s + 1
+// goes): each lane writes slot s before it reads slot s + 1, so the chain runs in place.
 __global__ __launch_bounds__(256) void carry_kernel(ScanParams p) {
   const int64_t BDN = p.Bsz * p.Dm * p.N;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;

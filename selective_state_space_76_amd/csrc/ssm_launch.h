@@ -20,7 +20,8 @@ struct ScanParams {
   void* out;
   float* final_state;
   float* ckpt;           // [B,nb,D,N] state entering each 64-step block (checkpoint pass), or null
-  float* seg_state;      // [S-1,B,D,N] end state of each segment scanned from zero
+  float* seg_state;      // [S-1,B,D,N] end state of each segment scanned from zero (the library
+                         // places it at carries + B*D*N; the carry pass overwrites it in place)
   float* seg_dsum;       // [S-1,B,D] sum of the step sizes of each segment
   int64_t Bsz, Dm, N, L;
   int64_t seg_len;       // steps per segment, a multiple of 64
@@ -114,7 +115,7 @@ hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
 // Size of the static per-device scratch array behind ssm_scan_fwd_noalloc, and its device address
 // on the device `stream` belongs to (the current device for the null stream), looked up once per
 // device.
-constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr size_t kScratchBytes = size_t(5) << 20;
 hipError_t scratch_buffer(hipStream_t stream, void** ptr);
 
 }  // namespace ssm

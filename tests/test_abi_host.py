@@ -109,7 +109,8 @@ def test_workspace_size_formula():
     lib = L.load()
     bdn, bd = 1024 * 16, 1024
     r = lambda x: (x + 255) // 256 * 256
-    want = lambda S: r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn)
+    # carries [S,B,D,N] (segment end states written into them in place) + step-size sums [S-1,B,D]
+    want = lambda S: r(4 * S * bdn) + r(4 * (S - 1) * bd)
     # lanes over states (fp32 streams, or ZOH): 64 channel blocks of 16 -> 16 segments of 65536 steps
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, io_dtype=L.SSM_F32)
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
@@ -124,11 +125,11 @@ def test_workspace_size_formula():
     s = shp(batch=1, dim=1000, dstate=16, seqlen=1 << 20)
     b1, b2 = 1000 * 16, 1000
     S = 64  # 16 groups
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * b1) + r(4 * (S - 1) * b2) + r(4 * S * b1)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=100, dstate=16, seqlen=1 << 16)
     S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 147 segments wanted, held to 1024 steps each
     b1, b2 = 100 * 16, 100
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * b1) + r(4 * (S - 1) * b2) + r(4 * S * b1)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=(1 << 20) - 4)
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
     # 2^24 steps: 64 rows of a stream pass 2^31 bytes, lanes over states (4 blocks of 16 channels
@@ -136,7 +137,7 @@ def test_workspace_size_formula():
     s = shp(batch=1, dim=64, dstate=16, seqlen=1 << 24)
     b1, b2 = 64 * 16, 64
     S = 256
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * (S - 1) * b1) + r(4 * (S - 1) * b2) + r(4 * S * b1)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
 
 
 def test_bwd_workspace_size_split():
@@ -148,7 +149,7 @@ def test_bwd_workspace_size_split():
     bdn, bd = 20 * 16, 20
     r = lambda x: (x + 255) // 256 * 256
     want = (r(4 * bdn * nbk) + r(4 * 2 * nblk * 16 * 5000) + r(4 * S * bdn) + r(4 * 2 * S * bd)
-            + r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + 3 * r(4 * S * bdn) + r(4 * S * bd))
+            + r(4 * (S - 1) * bd) + 3 * r(4 * S * bdn) + r(4 * S * bd))
     assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) == want
     # enough channels: no split, the plain layout
     s = shp(batch=8, dim=1536, dstate=16, seqlen=2048)
@@ -304,12 +305,12 @@ def test_saved_checkpoint_entry_points():
     s = shp(batch=1, dim=20, dstate=16, seqlen=5000)  # split: 5 segments
     S, bdn, bd = 5, 320, 20
     assert (lib.ssm_scan_bwd_workspace_size(ctypes.byref(s)) - lib.ssm_scan_bwd_saved_workspace_size(ctypes.byref(s))
-            == r(4 * bdn * ((5000 + 63) // 64)) + r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn))
+            == r(4 * bdn * ((5000 + 63) // 64)) + r(4 * (S - 1) * bd) + r(4 * S * bdn))
 
 
 def test_noalloc_errors_before_any_launch():
     """ssm_scan_fwd_noalloc checks every argument on the host first, then its scratch limit (a
-    split that needs more than its 8 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
+    split that needs more than its 5 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
     lib = L.load()
 
     def call(shape, **kw):

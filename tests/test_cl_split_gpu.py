@@ -36,7 +36,7 @@ def check_plan(Bsz, Dm, N, L):
     assert S is not None and S > 1
     r = lambda x: (x + 255) // 256 * 256
     bdn, bd = Bsz * Dm * N, Bsz * Dm
-    assert workspace_size(Bsz, Dm, N, L) == r(4 * (S - 1) * bdn) + r(4 * (S - 1) * bd) + r(4 * S * bdn)
+    assert workspace_size(Bsz, Dm, N, L) == r(4 * S * bdn) + r(4 * (S - 1) * bd)
     return S
 
 
