@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanPar
   const bf16_t* sd = stt + (0 * 64 + chl) * kClSP;  // this channel's delta row
   const bf16_t* su = stt + (1 * 64 + chl) * kClSP;  // u row
   const bf16_t* sz = stt + (MODE == 0 && GATE ? 2 * 64 + chl : 0) * kClSP;  // z row (output pass)
-  bf16_t* orow = reinterpret_cast<bf16_t*>(p.out) + (b * Dm + dd) * L;
+  bf16_t* sdw = stt + (0 * 64 + chl) * kClSP;  // the delta row again: the output pass's outputs
   float dsum = 0.0f, dcomp = 0.0f;  // Kahan sum of this lane's step sizes (summary pass)
 
   // One 64-step block; WHOLE: all 64 steps lie inside the segment, else the sequence's ragged last
@@ -254,15 +254,25 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanPar
           o[jj] = y + Dd * uu[jj];
           if (GATE) o[jj] *= silu_(zz[jj]);
         }
-        const int64_t t = t0 + jo;  // first of the row's 4 output steps
-        if (dval) {
-          if (WHOLE || jo + 4 <= rem) {
-            if (REV) *reinterpret_cast<uint2*>(orow + (L - 4 - t)) = make_uint2(pack_bf16(o[3], o[2]), pack_bf16(o[1], o[0]));
-            else *reinterpret_cast<uint2*>(orow + t) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
-          } else {
+        // into this channel's delta row, whose steps of this sub-block every row has read
+        *reinterpret_cast<uint2*>(sdw + jo) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+      }
+    }
+    if constexpr (MODE == 0) {
+      // the wave's 16 channels x 64 outputs, whole 16-byte pieces: lanes 8 i .. 8 i + 7 write one
+      // channel's row, so every store fills whole lines (pieces past the segment are not stored)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              if (jo + jj < rem) store_io(orow + (REV ? (L - 1 - t - jj) : t + jj), o[jj]);
+      for (int i = 0; i < 2; ++i) {
+        const int pc = lane + 64 * i, row = pc >> 3, cp = (pc & 7) * 8;
+        const int64_t dw = (int64_t)cg * 64 + 16 * w + row;
+        uint4 v = *reinterpret_cast<const uint4*>(stt + (16 * w + row) * kClSP + cp);
+        if (dw < Dm && (WHOLE || cp < rem)) {
+          bf16_t* op = reinterpret_cast<bf16_t*>(p.out) + (b * Dm + dw) * L;
+          if (REV) {
+            v = make_uint4(swap_halves(v.w), swap_halves(v.z), swap_halves(v.y), swap_halves(v.x));
+            *reinterpret_cast<uint4*>(op + (L - 8 - (t0 + cp))) = v;
+          } else {
+            *reinterpret_cast<uint4*>(op + t0 + cp) = v;
           }
         }
       }
