@@ -9,9 +9,9 @@
 //
 // Per 64-step block the workgroup stages B (and C) as fp32, shared by its 64 channels, and delta,
 // u (and z) of its channels as raw bf16 in LDS.  Per 16-step sub-block, row r forms dt and dt u
-// for steps r, r + 4, r + 8, r + 12 of its channel, each once; a permlane32 and two
-// permlane16 swaps hand every row the four rows' values, 4 consecutive steps at a time, and each
-// lane runs its 4 states' recurrences over those steps.  y = sum_n C h: the lane's 4 states in
+// for steps r, r + 4, r + 8, r + 12 of its channel, each once; the four rows' values pass through a
+// small per-wave LDS area, so every row reads 4 consecutive steps at a time, and each lane runs its
+// 4 states' recurrences over those steps.  y = sum_n C h: the lane's 4 states in
 // order, then the 4 rows' partial sums over two permlane-swap stages (a fixed order), which leave
 // row r with steps 4 r .. 4 r + 3 of the sub-block; it finishes them (D skip, gate, bf16 store).
 //
@@ -31,17 +31,6 @@ namespace {
 constexpr int kClTS = 68;  // fp32 B/C tile row: 64 steps + 4 pad
 constexpr int kClSP = 72;  // bf16 stream tile row: 64 steps + 8 pad (rows stay 16-byte aligned)
 
-// o[k] = the value v holds in row k of the wave (same column), in every row
-__device__ __forceinline__ void rows_allgather(float v, float (&o)[4]) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const auto a = __builtin_amdgcn_permlane16_swap(p[0], p[0], false, false);
-  const auto c = __builtin_amdgcn_permlane16_swap(p[1], p[1], false, false);
-  o[0] = __uint_as_float(a[0]);
-  o[1] = __uint_as_float(a[1]);
-  o[2] = __uint_as_float(c[0]);
-  o[3] = __uint_as_float(c[1]);
-}
-
 __device__ __forceinline__ uint32_t swap_halves(uint32_t v) { return (v >> 16) | (v << 16); }
 __device__ __forceinline__ float bf_at(const bf16_t* row, int j) { return __uint_as_float((uint32_t)row[j] << 16); }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -60,6 +49,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanPar
   constexpr int CPT = 1 + 2 * NS;                     // wave-chunks per wave
   __shared__ __attribute__((aligned(16))) float bct[NT * 16 * kClTS];
   __shared__ __attribute__((aligned(16))) bf16_t stt[NS * 64 * kClSP];
+  __shared__ __attribute__((aligned(16))) float xch[4 * 2 * 64];  // per wave: dt, dt u as [c][row]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -206,11 +196,18 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanPar
         }
       }
       float acc[16];
+      float* xw = xch + 128 * w;  // this wave's exchange slots
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float D4[4], X4[4];  // steps 4 q .. 4 q + 3 of the sub-block
-        rows_allgather(dq[q], D4);
-        rows_allgather(xq[q], X4);
+        // steps 4 q .. 4 q + 3 of the sub-block: row r's value of step 4 q + r goes to slot 4 c + r,
+        // and every lane of column c reads the 4 slots back as one 16-byte load.  Only this wave
+        // uses these slots, and a wave's LDS accesses complete in order, so no barrier is needed.
+        xw[4 * c + r] = dq[q];
+        xw[64 + 4 * c + r] = xq[q];
+        const float4 d4 = *reinterpret_cast<const float4*>(xw + 4 * c);
+        const float4 x4 = *reinterpret_cast<const float4*>(xw + 64 + 4 * c);
+        const float D4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float X4[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float4 bq = *reinterpret_cast<const float4*>(bct + (4 * r + k) * kClTS + 16 * s + 4 * q);
