@@ -473,11 +473,20 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float dj[16], xj[16], pj[16];
-        static_for<0, 16>([&](auto j_) {
-          constexpr int j = decltype(j_)::value;
-          dj[j] = row_bcast<j>(dl[s]);
-          xj[j] = row_bcast<j>(xu[s]);
-        });
+        // the row's 16 lanes have read their steps of this channel's delta and u rows (above), so
+        // they overwrite sub-block s with dt and dt u and read all 16 back; only this row reads
+        // these two rows and a wave's LDS accesses complete in order, so no barrier is needed
+        float* dw = const_cast<float*>(dch) + 16 * s;
+        float* xw = const_cast<float*>(uch) + 16 * s;
+        dw[g] = dl[s];
+        xw[g] = xu[s];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 vd = *reinterpret_cast<const float4*>(dw + 4 * q);
+          const float4 vx = *reinterpret_cast<const float4*>(xw + 4 * q);
+          dj[4 * q] = vd.x; dj[4 * q + 1] = vd.y; dj[4 * q + 2] = vd.z; dj[4 * q + 3] = vd.w;
+          xj[4 * q] = vx.x; xj[4 * q + 1] = vx.y; xj[4 * q + 2] = vx.z; xj[4 * q + 3] = vx.w;
+        }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           float hi = h[i];
