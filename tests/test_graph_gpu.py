@@ -66,8 +66,8 @@ def test_decode_steps_in_graph_match_eager():
         assert torch.equal(hs, ref_h) and torch.equal(cs, ref_c), rep
 
 
-@pytest.mark.parametrize("Bsz,Dm,N,L", [(2, 64, 16, 300), (1, 20, 16, 5000), (1, 20, 64, 4100)],
-                         ids=["whole", "split16", "split64"])
+@pytest.mark.parametrize("Bsz,Dm,N,L", [(2, 64, 16, 300), (1, 20, 16, 5000), (1, 20, 64, 4100), (1, 128, 16, 4096)],
+                         ids=["whole", "split16", "split64", "split16_channels_on_lanes"])
 def test_training_step_in_graph_matches_eager(Bsz, Dm, N, L):
     """conv1d + SiLU, the scan and its backward (with the sequence split where the shape asks
     for it) captured once and replayed: every output bit for bit equal to the eager call."""
