@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanPar
   const bf16_t* su = stt + (1 * 64 + chl) * kClSP;  // u row
   const bf16_t* sz = stt + (MODE == 0 && GATE ? 2 * 64 + chl : 0) * kClSP;  // z row (output pass)
   bf16_t* sdw = stt + (0 * 64 + chl) * kClSP;  // the delta row again: the output pass's outputs
-  float dsum = 0.0f, dcomp = 0.0f;  // Kahan sum of this lane's step sizes (summary pass)
+  float dsum = 0.0f, dcomp = 0.0f;  // Kahan sum of this row's step sizes (summary pass)
 
   // One 64-step block; WHOLE: all 64 steps lie inside the segment, else the sequence's ragged last
   // block, whose steps past the end are identity steps (see fetch) and are not stored
@@ -189,11 +189,12 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanPar
         const float dt = softplus_(bf_at(sd, j) + biasd);
         dq[q] = dt;
         xq[q] = dt * uu;
-        if (MODE == 1) {
-          const float yk = dt - dcomp, tk = dsum + yk;
-          dcomp = (tk - dsum) - yk;
-          dsum = tk;
-        }
+      }
+      if (MODE == 1) {  // the row's 4 steps of the sub-block, then one compensated add
+        const float part = (dq[0] + dq[1]) + (dq[2] + dq[3]);
+        const float yk = part - dcomp, tk = dsum + yk;
+        dcomp = (tk - dsum) - yk;
+        dsum = tk;
       }
       float acc[16];
       float* xw = xch + 128 * w;  // this wave's exchange slots
