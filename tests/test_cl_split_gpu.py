@@ -4,6 +4,7 @@ L a multiple of 8) against the fp64 oracle, element by element (GPU).
 Each shape is chosen so that the forward plan takes this layout: whole and ragged 64-channel
 groups, ragged last blocks, a last segment of one partial block, fewer than 16 states, missing
 optional operands, the backward-in-time direction, an initial state and many segments."""
+import numpy as np
 import pytest
 import torch
 
@@ -93,3 +94,28 @@ def test_cl_split_many_segments():
     print("case: channels on lanes %s, %d segments" % (shape, S), flush=True)
     h0 = torch.randn(1, 64, 16, generator=torch.Generator().manual_seed(3))
     full_check(make(*shape, seed=23), h0=h0)
+
+
+def _cl_draws(n, seed=76077):
+    """Seeded shapes the plan runs with channels on lanes, with every option drawn at random."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        c = dict(B=int(rng.integers(1, 4)), D=int(rng.integers(54, 321)), N=int(rng.choice([1, 3, 8, 12, 16])),
+                 L=8 * int(rng.integers(256, 751)), reverse=bool(rng.integers(0, 2)), gate=bool(rng.integers(0, 2)),
+                 skip=bool(rng.integers(0, 2)), bias=bool(rng.integers(0, 2)), h0=bool(rng.integers(0, 2)),
+                 seed=int(rng.integers(0, 1 << 30)))
+        if segments(c["B"], c["D"], c["N"], c["L"]):
+            out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("c", _cl_draws(24), ids=lambda c: "%dx%dx%dx%d" % (c["B"], c["D"], c["N"], c["L"]))
+def test_cl_split_random(c):
+    S = check_plan(c["B"], c["D"], c["N"], c["L"])
+    print("case: channels on lanes random %s, %d segments" % (c, S), flush=True)
+    x = make(c["B"], c["D"], c["N"], c["L"], seed=c["seed"] % 100000, gate=c["gate"], skip=c["skip"], bias=c["bias"])
+    h0 = None
+    if c["h0"]:
+        h0 = torch.randn(c["B"], c["D"], c["N"], generator=torch.Generator().manual_seed(c["seed"]))
+    full_check(x, h0=h0, reverse=c["reverse"])
