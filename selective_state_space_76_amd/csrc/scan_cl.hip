@@ -40,8 +40,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // MODE 0: output pass from the carried state (writes out; the last segment also final_state).
 // MODE 1: summary pass over segments 0..S-2 (writes seg_state and seg_dsum).
 // GATE: the output pass multiplies by silu(z).
-// 4 workgroups (waves per SIMD) for the output pass (128 VGPRs: its chains, C h sums and prefetch
-// registers), 5 for the summary pass.
+// 4 workgroups (waves per SIMD) for the output pass (its chains, C h sums and prefetch registers
+// need up to 128 VGPRs), 5 for the summary pass.
 template <int MODE, bool REV, bool GATE>
 __global__ __launch_bounds__(256, MODE == 0 ? 4 : 5) void scan_cl_kernel(ScanParams p) {
   constexpr int NT = MODE == 0 ? 2 : 1;               // staged coefficient tensors: B (and C)

@@ -14,8 +14,7 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 40;
 constexpr int64_t kMaxElems = int64_t(1) << 61;
-constexpr int kTargetBlocks = 1024;    // 4 workgroups of 4 waves per CU on 256 CUs
-constexpr int kTargetBlocksCl = 1024;  // 4 output-pass workgroups per CU on 256 CUs (channels on lanes)
+constexpr int kTargetBlocks = 1024;    // output-pass workgroups of 4 waves: 4 per CU on 256 CUs
 constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
 
 struct Range {
@@ -69,9 +68,8 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
     const int64_t pad = (s->dim + 63) / 64 * 64 - s->dim;
     pl->cl = s->io_dtype == SSM_BF16 && !(s->flags & SSM_FLAG_ZOH) && s->dstate <= 16 && L % 8 == 0 &&
              L < (int64_t(1) << 24) && 5 * pad <= s->dim;
-    const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;
-    const int64_t target = pl->cl ? kTargetBlocksCl : kTargetBlocks;
-    const int64_t want = (target + units - 1) / units;
+    const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;  // workgroups per segment
+    const int64_t want = (kTargetBlocks + units - 1) / units;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 63) / 64) * 64;
     if (seg < kMinSegment) seg = kMinSegment;
