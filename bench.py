@@ -519,6 +519,64 @@ def issue_probe():
                     "v_exp_f32 and DPP-sourced operations issue at a fraction of it"}
 
 
+def tp_library():
+    """The scan in the time-parallel layout, built beside the scan library (None if it is not built)."""
+    path = os.path.join(ROOT, "selective_state_space_76_amd", "libssmtp.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.ssm_tp_scan_fwd.argtypes = [i64, i64, i64, i64] + [vp] * 12
+    lib.ssm_tp_scan_fwd.restype = ctypes.c_int
+    return lib
+
+
+def tp_scan_fwd(torch, lib, g, out, final_state=None, init=None):
+    """out (and final_state) from the time-parallel scan on torch's current stream; g holds the
+    scan inputs as device tensors (bf16 streams)."""
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    Bsz, Dm, L = g["u"].shape
+    rc = lib.ssm_tp_scan_fwd(Bsz, Dm, g["A"].shape[1], L, p(g["u"]), p(g["delta"]), p(g["A"]), p(g["B"]),
+                             p(g["C"]), p(g.get("D")), p(g.get("z")), p(g.get("delta_bias")), p(init), p(out),
+                             p(final_state), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError("ssm_tp_scan_fwd returned %d" % rc)
+
+
+def bench_layouts(torch, ssm, W, name="mamba130m", calls=20):
+    """The library's scan against the same scan in the time-parallel layout (the pages' associative
+    scan over time), same inputs, HIP events around each call."""
+    lib = tp_library()
+    if lib is None:
+        return None
+    w = W.WORKLOADS[name]
+    g = W.scan_inputs(w, device="cuda")
+    out = torch.empty_like(g["u"])
+    fs = torch.empty(w.batch, w.dim, w.dstate, device="cuda")
+    runs = {
+        "library": lambda: ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"],
+                                        out=out, final_state=fs),
+        "time_parallel": lambda: tp_scan_fwd(torch, lib, g, out, fs),
+    }
+    res = {"workload": "%s shape (%d x %d x %d x %d), bf16" % (name, w.batch, w.dim, w.dstate, w.seqlen)}
+    for k, f in runs.items():
+        for _ in range(3):
+            f()
+        ts = []
+        for _ in range(calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        res[k + "_call_ms_median"] = ts[len(ts) // 2]
+    res["note"] = ("the time-parallel layout: lanes over time, a row_shr DPP scan of (A_bar, B_bar u) pairs "
+                   "over each row, states in a loop; the library keeps states on lanes and time sequential")
+    return res
+
+
 def input_digest(torch, x):
     """fp64 sums of every input and a 64-bit hash of its first 16 MiB (its bytes as stored)."""
     sums, hashes = {}, {}
@@ -544,6 +602,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-layout", action="store_true", help="skip the time-parallel layout comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -630,6 +689,13 @@ def main():
         dec["roofline"]["frac_of_copy_peak"] = dec["roofline"]["achieved"] / cp
         res["conv1d"] = pre
         res["conv1d_update"] = dec
+    if not args.no_layout:
+        lay = bench_layouts(torch, ssm, W)
+        if lay is not None:
+            res["layout_alternative"] = lay
+            log("layouts (%s): library %.4f ms, time-parallel %.4f ms per call"
+                % (lay["workload"], lay["library_call_ms_median"], lay["time_parallel_call_ms_median"]))
+        torch.cuda.empty_cache()
     if not args.no_probe:
         pr = issue_probe()
         if pr is not None:

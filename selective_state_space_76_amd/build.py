@@ -43,6 +43,8 @@ def _compile_cmd(src: str, obj: str):
 
 PROBE_SRC = os.path.join(CSRC, "issue_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libssmprobe.so")
+TP_SRC = os.path.join(CSRC, "scan_time_parallel.hip")
+TP_LIB = os.path.join(PKG, "libssmtp.so")
 
 
 def build_probe(verbose: bool = False) -> str:
@@ -56,6 +58,20 @@ def build_probe(verbose: bool = False) -> str:
         raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), r.stdout))
     os.replace(tmp, PROBE_LIB)
     return PROBE_LIB
+
+
+def build_tp(verbose: bool = False) -> str:
+    """The scan in the time-parallel layout, which bench.py times beside the library's (a separate
+    library, not the ABI)."""
+    tmp = TP_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-shared", TP_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), r.stdout))
+    os.replace(tmp, TP_LIB)
+    return TP_LIB
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
@@ -91,3 +107,4 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
     print(build_probe(verbose="-v" in sys.argv))
+    print(build_tp(verbose="-v" in sys.argv))
