@@ -13,8 +13,9 @@ rotated through enough independent sets that they cannot be served from the
 256 MB Infinity Cache.  The same JSON line carries the decode path
 (ssm_state_update) on the 2.8B-shaped generation workload, the backward pass
 (ssm_scan_bwd) on the two layer shapes, the conv + SiLU step that produces u,
-a probe of the VALU issue rate, and the fp64 CPU oracle's rate on a bounded
-sample of the headline workload.
+the 130M-shaped scan in the time-parallel layout beside the library's (the
+layout comparison), a probe of the VALU issue rate, and the fp64 CPU oracle's
+rate on a bounded sample of the headline workload.
 
 Progress goes to stderr; stdout gets exactly one JSON line.
 """
