@@ -70,3 +70,11 @@ def test_counter_files_for_every_record(name, monkeypatch):
     assert bench.traffic_from_profile(name, 1) == c["hbm_bytes_per_launch"]
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.traffic_from_profile(name, 1) is None
+
+
+def test_time_parallel_library_is_built_and_exports_its_entry():
+    """The layout comparison's library: built beside the scan library (build() compiles it) and
+    loadable without a GPU."""
+    lib = bench.tp_library()
+    assert lib is not None
+    assert hasattr(lib, "ssm_tp_scan_fwd")
