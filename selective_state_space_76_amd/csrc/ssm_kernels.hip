@@ -43,19 +43,32 @@ hipError_t scratch_buffer(hipStream_t stream, void** ptr) {
 
 // Chains the segment summaries: carries[s] is the state entering segment s.  seg_state may lie in
 // the carries' own slots 1 .. S-1 (segment s's end state where the state entering segment s + 1
-// goes): each lane writes slot s before it reads slot s + 1, so the chain runs in place.
+// goes).  The summaries are read 8 segments at a time before the chain over them runs, so a lane's
+// loads are not serialised behind its stores; every slot is read before it is overwritten, so the
+// chain also runs in place.
 __global__ __launch_bounds__(256) void carry_kernel(ScanParams p) {
+  constexpr int G = 8;
   const int64_t BDN = p.Bsz * p.Dm * p.N;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= BDN) return;
   const int64_t n = idx % p.N, bd = idx / p.N, d = bd % p.Dm;
   const float Ap = p.A[d * p.N + n] * kLog2e;
   float hc = p.init ? p.init[idx] : 0.0f;
-  for (int s = 0; s < p.S; ++s) {
-    p.carries[(int64_t)s * BDN + idx] = hc;
-    if (s + 1 < p.S) {
-      const float decay = exp2_(Ap * p.seg_dsum[(int64_t)s * p.Bsz * p.Dm + bd]);
-      hc = __builtin_fmaf(decay, hc, p.seg_state[(int64_t)s * BDN + idx]);
+  for (int s0 = 0; s0 < p.S; s0 += G) {
+    float st[G], ds[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {  // the end states and step-size sums of segments s0 .. s0 + G - 1
+      const int s = s0 + k;
+      st[k] = s + 1 < p.S ? p.seg_state[(int64_t)s * BDN + idx] : 0.0f;
+      ds[k] = s + 1 < p.S ? p.seg_dsum[(int64_t)s * p.Bsz * p.Dm + bd] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int s = s0 + k;
+      if (s < p.S) {
+        p.carries[(int64_t)s * BDN + idx] = hc;
+        if (s + 1 < p.S) hc = __builtin_fmaf(exp2_(Ap * ds[k]), hc, st[k]);
+      }
     }
   }
 }
