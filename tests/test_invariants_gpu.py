@@ -27,7 +27,8 @@ def run(x, **kw):
     return out, fs
 
 
-@pytest.mark.parametrize("shape", [(2, 40, 16, 1000), (1, 24, 16, 5000), (2, 20, 64, 700)], ids=str)
+@pytest.mark.parametrize("shape", [(2, 40, 16, 1000), (1, 24, 16, 5000), (2, 20, 64, 700), (1, 64, 16, 4096)],
+                         ids=str)
 def test_deterministic(shape):
     print("case: determinism", shape, flush=True)
     x = inputs(*shape)
@@ -36,7 +37,7 @@ def test_deterministic(shape):
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
-@pytest.mark.parametrize("shape", [(2, 40, 16, 1000), (1, 24, 16, 5000)], ids=str)
+@pytest.mark.parametrize("shape", [(2, 40, 16, 1000), (1, 24, 16, 5000), (1, 64, 16, 4096)], ids=str)
 @pytest.mark.parametrize("reverse", [False, True])
 def test_causal_bitwise(shape, reverse):
     """Perturbing every input at step s leaves all outputs before s (after s when reversed) unchanged."""
@@ -76,11 +77,13 @@ def test_permutation_equivariance_bitwise():
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-def test_split_matches_unsplit(dtype):
-    """Few channels, long sequence: the three-pass split equals the single sequential pass."""
-    print("case: split vs unsplit", dtype, flush=True)
-    x = inputs(1, 32, 16, 9000, dtype=dtype, seed=3)
-    assert workspace_size(1, 32, 16, 9000) > 0
+@pytest.mark.parametrize("Dm", [32, 64], ids=["lanes_over_states", "channels_on_lanes"])
+def test_split_matches_unsplit(dtype, Dm):
+    """Few channels, long sequence: the three-pass split equals the single sequential pass (with bf16
+    streams and D = 64 the split's passes keep channels on lanes)."""
+    print("case: split vs unsplit", dtype, Dm, flush=True)
+    x = inputs(1, Dm, 16, 9000, dtype=dtype, seed=3)
+    assert workspace_size(1, Dm, 16, 9000) > 0
     o1, f1 = run(x)
     o2, f2 = run(x, split=False)
     tol = 1e-4 if dtype == torch.float32 else 2e-2
@@ -140,7 +143,8 @@ def test_small_step_limit():
 
 
 def test_full_workload_determinism_and_split_plan():
-    """The 1M-step DNA shape runs split into 16 segments; two runs agree bit for bit."""
+    """The DNA shape at 2^18 steps runs split (64 segments, channels on lanes); two runs agree bit for
+    bit."""
     w = W.WORKLOADS["dna1m"].with_shape(seqlen=1 << 18)
     print("case: long split determinism", flush=True)
     x = W.scan_inputs(w, device=DEV)
