@@ -8,7 +8,10 @@ import numpy as np
 import pytest
 import torch
 
-from selective_state_space_76_amd import workspace_size
+import oracle
+
+from selective_state_space_76_amd import scan_fwd, workspace_size
+from tests.gpu_util import rel_err
 from tests.test_parity_gpu import full_check, make
 
 pytestmark = pytest.mark.gpu
@@ -119,3 +122,48 @@ def test_cl_split_random(c):
     if c["h0"]:
         h0 = torch.randn(c["B"], c["D"], c["N"], generator=torch.Generator().manual_seed(c["seed"]))
     full_check(x, h0=h0, reverse=c["reverse"])
+
+
+def _wide_draws(n, seed=2026):
+    """Channels-on-lanes shapes with the wide value spreads of the fp32 extreme-value tests."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append(dict(B=int(rng.integers(1, 3)), D=int(rng.choice([64, 128, 300])), N=int(rng.choice([1, 4, 16])),
+                        L=8 * int(rng.integers(256, 513)), reverse=bool(rng.integers(0, 2)),
+                        u_scale=float(10 ** rng.uniform(-2, 2)), d_span=float(rng.uniform(1, 60)),
+                        d_shift=float(rng.uniform(0, 30)), b_scale=float(10 ** rng.uniform(-1, 1)),
+                        c_scale=float(10 ** rng.uniform(-1, 1)), skip=bool(rng.integers(0, 2)),
+                        gate=bool(rng.integers(0, 2)), bias=bool(rng.integers(0, 2)), h0=bool(rng.integers(0, 2)),
+                        seed=int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("c", _wide_draws(12), ids=lambda c: "%dx%dx%dx%d" % (c["B"], c["D"], c["N"], c["L"]))
+def test_cl_split_wide_values(c):
+    """A from -1e4 to -1e-6 with exact zeros, delta + bias up to +-30, u, B and C over decades, the gate
+    over [-50, 50], bf16 streams, against the oracle at the bf16 bound.  Not held to one ulp: with
+    these spreads a state can be a near-constant chain over thousands of steps, whose fp32 rounding
+    alone reaches an ulp of the small outputs."""
+    check_plan(c["B"], c["D"], c["N"], c["L"])
+    print("case: channels on lanes wide values %s" % c, flush=True)
+    B, D, N, L = c["B"], c["D"], c["N"], c["L"]
+    g = torch.Generator().manual_seed(c["seed"])
+    bf = lambda t: t.to(torch.bfloat16)
+    u = bf(torch.randn(B, D, L, generator=g) * c["u_scale"])
+    delta = bf(torch.rand(B, D, L, generator=g) * c["d_span"] - c["d_shift"])
+    A = -(10 ** (torch.rand(D, N, generator=g) * 10 - 6))
+    A[torch.rand(D, N, generator=g) < 0.1] = 0.0
+    Bm = bf(torch.randn(B, N, L, generator=g) * c["b_scale"])
+    Cm = bf(torch.randn(B, N, L, generator=g) * c["c_scale"])
+    Dv = torch.randn(D, generator=g) if c["skip"] else None
+    z = bf(torch.rand(B, D, L, generator=g) * 100 - 50) if c["gate"] else None
+    bias = torch.randn(D, generator=g) if c["bias"] else None
+    h0 = torch.randn(B, D, N, generator=g) if c["h0"] else None
+    dv = lambda t: None if t is None else t.to("cuda")
+    out, fs = scan_fwd(dv(u), dv(delta), dv(A), dv(Bm), dv(Cm), dv(Dv), dv(z), dv(bias), dv(h0), reverse=c["reverse"])
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(u, delta, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, h0=h0, reverse=c["reverse"])
+    ey, eh = rel_err(out, ry), rel_err(fs, rh)
+    print("rel_err y=%.3g state=%.3g" % (ey, eh), flush=True)
+    assert ey <= 2e-2 and eh <= 2e-2, (ey, eh)
