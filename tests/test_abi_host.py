@@ -330,3 +330,31 @@ def test_noalloc_errors_before_any_launch():
     assert call(shp(flags=8)) == 5
     assert call(shp(), out=fake(1)) == 8  # out is u
     assert call(big, out=fake(1)) == 8    # argument errors come before the scratch limit
+
+
+@pytest.mark.parametrize("kw,cl", [
+    (dict(), True),                                   # bf16, default discretisation, N <= 16, L % 8 == 0
+    (dict(dstate=17), False),                         # more than 16 states
+    (dict(flags=L.SSM_FLAG_ZOH), False),              # zero-order hold
+    (dict(io_dtype=L.SSM_F32), False),                # fp32 streams
+    (dict(seqlen=(1 << 20) + 4), False),              # rows not whole 16-byte pieces
+    (dict(dim=159), False),                           # 33 of 192 channels padded: more than a fifth of 159
+    (dict(dim=160), True),                            # 32 of 192 padded: exactly a fifth of 160
+    (dict(flags=L.SSM_FLAG_REVERSE), True),           # the direction does not matter
+], ids=["base", "N17", "zoh", "fp32", "L_not_8", "pad_over_fifth", "pad_a_fifth", "reverse"])
+def test_split_layout_rule(kw, cl):
+    """Which layout the split's passes take, read from the segment count the workspace implies: with
+    channels on lanes the plan targets 1024 workgroups of 64 channels, otherwise 1024 of 16."""
+    lib = L.load()
+    args = dict(batch=1, dim=128, dstate=16, seqlen=1 << 20)  # long enough that the layouts' segment counts differ
+    args.update(kw)
+    s = shp(**args)
+    Bsz, Dm, N, Ln = args["batch"], args["dim"], args["dstate"], args["seqlen"]
+    r = lambda x: (x + 255) // 256 * 256
+    cdiv = lambda a, b: -(-a // b)
+    def segments(units):
+        seg = max(1024, cdiv(cdiv(Ln, cdiv(1024, units)), 64) * 64)
+        return cdiv(Ln, seg)
+    S, other = (segments(Bsz * cdiv(Dm, 64)), segments(Bsz * cdiv(Dm, 16)))[:: 1 if cl else -1]
+    assert S > 1 and S != other
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * Bsz * Dm * N) + r(4 * (S - 1) * Bsz * Dm)
