@@ -16,6 +16,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 40;
 constexpr int64_t kMaxElems = int64_t(1) << 61;
 constexpr int kTargetBlocks = 1024;    // output-pass workgroups of 4 waves: 4 per CU on 256 CUs
 constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
+// Channels on lanes: four rounds of output-pass workgroups (shorter segments balance the passes'
+// workgroups over the CUs), at most 256 segments (the carry pass is sequential over them).
+constexpr int kTargetBlocksCl = 4096;
+constexpr int64_t kMaxSegmentsCl = 256;
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -69,7 +73,9 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
     pl->cl = s->io_dtype == SSM_BF16 && !(s->flags & SSM_FLAG_ZOH) && s->dstate <= 16 && L % 8 == 0 &&
              L < (int64_t(1) << 24) && 5 * pad <= s->dim;
     const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;  // workgroups per segment
-    const int64_t want = (kTargetBlocks + units - 1) / units;
+    const int64_t target = pl->cl ? kTargetBlocksCl : kTargetBlocks;
+    int64_t want = (target + units - 1) / units;
+    if (pl->cl && want > kMaxSegmentsCl) want = kMaxSegmentsCl;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 63) / 64) * 64;
     if (seg < kMinSegment) seg = kMinSegment;
@@ -168,7 +174,7 @@ const char* ssm_status_str(int status) {
     case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_workspace_size()";
     case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SSM_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
-    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (5 MiB)";
+    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (17 MiB)";
     default: return "unknown status";
   }
 }

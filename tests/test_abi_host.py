@@ -117,14 +117,22 @@ def test_workspace_size_formula():
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, flags=L.SSM_FLAG_ZOH)
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
     # channels on lanes (bf16, default discretisation, N <= 16, L % 8 == 0, L < 2^24): 16 groups
-    # of 64 channels -> 64 segments of 16384 steps (1024 workgroups of the output pass)
+    # of 64 channels -> 4096 / 16 = 256 segments of 4096 steps (4096 workgroups of the output pass)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(256)
+    # 4 groups: 1024 segments wanted, held to 256
+    s = shp(batch=1, dim=256, dstate=16, seqlen=1 << 20)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 256 * 256 * 16) + r(4 * 255 * 256)
+    # 48 groups: 86 segments wanted, of 12224 steps (the last 9536)
+    s = shp(batch=3, dim=1024, dstate=16, seqlen=1 << 20)
+    S = -(-(1 << 20) // ((-(-(1 << 20) // 86) + 63) // 64 * 64))
+    assert S == 86
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * 3 * 1024 * 16) + r(4 * (S - 1) * 3 * 1024)
     # D = 1000 pads 24 channels to whole groups (under a fifth): still channels on lanes; D = 100
     # would pad 28 (over a fifth) and L not a multiple of 8 breaks the 16-byte rows: lanes over states
     s = shp(batch=1, dim=1000, dstate=16, seqlen=1 << 20)
     b1, b2 = 1000 * 16, 1000
-    S = 64  # 16 groups
+    S = 256  # 16 groups
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=100, dstate=16, seqlen=1 << 16)
     S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 147 segments wanted, held to 1024 steps each
@@ -310,7 +318,7 @@ def test_saved_checkpoint_entry_points():
 
 def test_noalloc_errors_before_any_launch():
     """ssm_scan_fwd_noalloc checks every argument on the host first, then its scratch limit (a
-    split that needs more than its 5 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
+    split that needs more than its 17 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
     lib = L.load()
 
     def call(shape, **kw):
@@ -319,8 +327,12 @@ def test_noalloc_errors_before_any_launch():
         return lib.ssm_scan_fwd_noalloc(None if shape is None else ctypes.byref(shape), p["u"], p["delta"], p["A"],
                                         p["B"], p["C"], None, None, None, None, p["out"], None, None)
 
-    big = shp(batch=1, dim=8000, dstate=64, seqlen=4096)
+    # 1 x 1152 x 16 x 2^20: 18 groups of 64 channels, 228 segments, 17.03 MiB; the DNA shape
+    # (1 x 1024 x 16 x 2^20, 256 segments) needs 16.996 MiB and fits
+    big = shp(batch=1, dim=1152, dstate=16, seqlen=1 << 20)
     assert L.load().ssm_scan_workspace_size(ctypes.byref(big)) > L.SCRATCH_BYTES
+    dna = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
+    assert L.load().ssm_scan_workspace_size(ctypes.byref(dna)) <= L.SCRATCH_BYTES
     assert call(big) == 9
     assert call(None) == 1
     assert call(shp(dstate=65)) == 2
@@ -344,7 +356,8 @@ def test_noalloc_errors_before_any_launch():
 ], ids=["base", "N17", "zoh", "fp32", "L_not_8", "pad_over_fifth", "pad_a_fifth", "reverse"])
 def test_split_layout_rule(kw, cl):
     """Which layout the split's passes take, read from the segment count the workspace implies: with
-    channels on lanes the plan targets 1024 workgroups of 64 channels, otherwise 1024 of 16."""
+    channels on lanes the plan targets 4096 workgroups of 64 channels (at most 256 segments),
+    otherwise 1024 of 16."""
     lib = L.load()
     args = dict(batch=1, dim=128, dstate=16, seqlen=1 << 20)  # long enough that the layouts' segment counts differ
     args.update(kw)
@@ -352,9 +365,9 @@ def test_split_layout_rule(kw, cl):
     Bsz, Dm, N, Ln = args["batch"], args["dim"], args["dstate"], args["seqlen"]
     r = lambda x: (x + 255) // 256 * 256
     cdiv = lambda a, b: -(-a // b)
-    def segments(units):
-        seg = max(1024, cdiv(cdiv(Ln, cdiv(1024, units)), 64) * 64)
+    def segments(units, target, cap):
+        seg = max(1024, cdiv(cdiv(Ln, min(cap, cdiv(target, units))), 64) * 64)
         return cdiv(Ln, seg)
-    S, other = (segments(Bsz * cdiv(Dm, 64)), segments(Bsz * cdiv(Dm, 16)))[:: 1 if cl else -1]
+    S, other = (segments(Bsz * cdiv(Dm, 64), 4096, 256), segments(Bsz * cdiv(Dm, 16), 1024, 1 << 40))[:: 1 if cl else -1]
     assert S > 1 and S != other
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * Bsz * Dm * N) + r(4 * (S - 1) * Bsz * Dm)

@@ -16,7 +16,7 @@ from tests.test_parity_gpu import full_check, make
 
 pytestmark = pytest.mark.gpu
 
-MIN_SEG, TARGET = 1024, 1024
+MIN_SEG, TARGET, MAX_SEGMENTS = 1024, 4096, 256
 
 
 def cdiv(a, b):
@@ -30,7 +30,7 @@ def segments(Bsz, Dm, N, L):
     if not (Bsz * cdiv(Dm, 16) < 512 and 2 * MIN_SEG <= L < 1 << 24 and L % 8 == 0 and N <= 16
             and 5 * (-Dm % 64) <= Dm):
         return None
-    want = cdiv(TARGET, Bsz * cdiv(Dm, 64))
+    want = min(MAX_SEGMENTS, cdiv(TARGET, Bsz * cdiv(Dm, 64)))
     seg = max(MIN_SEG, cdiv(cdiv(L, want), 64) * 64)
     return cdiv(L, seg)
 

@@ -143,8 +143,8 @@ def test_small_step_limit():
 
 
 def test_full_workload_determinism_and_split_plan():
-    """The DNA shape at 2^18 steps runs split (64 segments, channels on lanes); two runs agree bit for
-    bit."""
+    """The DNA shape at 2^18 steps runs split (256 segments, channels on lanes); two runs agree bit
+    for bit."""
     w = W.WORKLOADS["dna1m"].with_shape(seqlen=1 << 18)
     print("case: long split determinism", flush=True)
     x = W.scan_inputs(w, device=DEV)
