@@ -16,9 +16,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 40;
 constexpr int64_t kMaxElems = int64_t(1) << 61;
 constexpr int kTargetBlocks = 1024;    // output-pass workgroups of 4 waves: 4 per CU on 256 CUs
 constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
-// Channels on lanes: four rounds of output-pass workgroups (shorter segments balance the passes'
-// workgroups over the CUs), at most 256 segments (the carry pass is sequential over them).
-constexpr int kTargetBlocksCl = 4096;
+// A split aims at four rounds of output-pass workgroups: shorter segments balance the passes'
+// workgroups over the CUs.  With channels on lanes, at most 256 segments (the carry pass is
+// sequential over them) unless one round needs more.
+constexpr int kRounds = 4;
 constexpr int64_t kMaxSegmentsCl = 256;
 
 struct Range {
@@ -73,9 +74,9 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
     pl->cl = s->io_dtype == SSM_BF16 && !(s->flags & SSM_FLAG_ZOH) && s->dstate <= 16 && L % 8 == 0 &&
              L < (int64_t(1) << 24) && 5 * pad <= s->dim;
     const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;  // workgroups per segment
-    const int64_t target = pl->cl ? kTargetBlocksCl : kTargetBlocks;
-    int64_t want = (target + units - 1) / units;
-    if (pl->cl && want > kMaxSegmentsCl) want = kMaxSegmentsCl;
+    const int64_t one = (kTargetBlocks + units - 1) / units;                   // segments for one round
+    int64_t want = (kRounds * kTargetBlocks + units - 1) / units;
+    if (pl->cl && want > kMaxSegmentsCl) want = kMaxSegmentsCl > one ? kMaxSegmentsCl : one;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 63) / 64) * 64;
     if (seg < kMinSegment) seg = kMinSegment;
@@ -109,9 +110,9 @@ struct BwdPlan {
 constexpr int kBwdTargetBlocks = 768;  // 3 backward workgroups per CU on 256 CUs
 
 // Shape-only, like the forward's plan.  Few channels and a long sequence: split the sequence
-// into segments (whole 256-step chunks, >= 1024 steps) so that about kBwdTargetBlocks
-// workgroups run; each segment's checkpoints start from a carried state (summary pass + carry)
-// and its adjoint from a carried adjoint (adjoint summary + carry).
+// into segments (whole 256-step chunks, >= 1024 steps) so that about kRounds x kBwdTargetBlocks
+// workgroups run (four rounds); each segment's checkpoints start from a carried state (summary
+// pass + carry) and its adjoint from a carried adjoint (adjoint summary + carry).
 bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl, bool saved = false) {
   Plan fp;
   if (!make_plan(s, &fp)) return false;  // same size limits as the forward
@@ -122,7 +123,7 @@ bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl, bool saved = false) {
   pl->S = 1;
   pl->seg_len = ((L + 255) / 256) * 256;
   if (base < kBwdTargetBlocks / 2 && L >= 2 * kMinSegment) {
-    const int64_t want = (kBwdTargetBlocks + base - 1) / base;
+    const int64_t want = (kRounds * kBwdTargetBlocks + base - 1) / base;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 255) / 256) * 256;
     if (seg < kMinSegment) seg = kMinSegment;

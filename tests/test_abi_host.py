@@ -111,18 +111,22 @@ def test_workspace_size_formula():
     r = lambda x: (x + 255) // 256 * 256
     # carries [S,B,D,N] (segment end states written into them in place) + step-size sums [S-1,B,D]
     want = lambda S: r(4 * S * bdn) + r(4 * (S - 1) * bd)
-    # lanes over states (fp32 streams, or ZOH): 64 channel blocks of 16 -> 16 segments of 65536 steps
+    # lanes over states (fp32 streams, or ZOH): 64 channel blocks of 16 -> 4 x 1024 / 64 = 64 segments
+    # of 16384 steps (four rounds of output-pass workgroups)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, io_dtype=L.SSM_F32)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, flags=L.SSM_FLAG_ZOH)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
     # channels on lanes (bf16, default discretisation, N <= 16, L % 8 == 0, L < 2^24): 16 groups
     # of 64 channels -> 4096 / 16 = 256 segments of 4096 steps (4096 workgroups of the output pass)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(256)
-    # 4 groups: 1024 segments wanted, held to 256
+    # 4 groups: 1024 segments wanted, held to 256 (one round's count)
     s = shp(batch=1, dim=256, dstate=16, seqlen=1 << 20)
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 256 * 256 * 16) + r(4 * 255 * 256)
+    # 2 groups: 2048 wanted, held to 512, the count of one round (no fewer segments than one round)
+    s = shp(batch=1, dim=128, dstate=16, seqlen=1 << 20)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 512 * 128 * 16) + r(4 * 511 * 128)
     # 48 groups: 86 segments wanted, of 12224 steps (the last 9536)
     s = shp(batch=3, dim=1024, dstate=16, seqlen=1 << 20)
     S = -(-(1 << 20) // ((-(-(1 << 20) // 86) + 63) // 64 * 64))
@@ -135,16 +139,16 @@ def test_workspace_size_formula():
     S = 256  # 16 groups
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=100, dstate=16, seqlen=1 << 16)
-    S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 147 segments wanted, held to 1024 steps each
+    S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 586 segments wanted, held to 1024 steps each
     b1, b2 = 100 * 16, 100
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=(1 << 20) - 4)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(16)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
     # 2^24 steps: 64 rows of a stream pass 2^31 bytes, lanes over states (4 blocks of 16 channels
-    # -> 256 segments of 65536 steps; channels on lanes would take 1024)
+    # -> 1024 segments of 16384 steps)
     s = shp(batch=1, dim=64, dstate=16, seqlen=1 << 24)
     b1, b2 = 64 * 16, 64
-    S = 256
+    S = 1024
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
 
 
@@ -355,19 +359,22 @@ def test_noalloc_errors_before_any_launch():
     (dict(flags=L.SSM_FLAG_REVERSE), True),           # the direction does not matter
 ], ids=["base", "N17", "zoh", "fp32", "L_not_8", "pad_over_fifth", "pad_a_fifth", "reverse"])
 def test_split_layout_rule(kw, cl):
-    """Which layout the split's passes take, read from the segment count the workspace implies: with
-    channels on lanes the plan targets 4096 workgroups of 64 channels (at most 256 segments),
-    otherwise 1024 of 16."""
+    """Which layout the split's passes take, read from the segment count the workspace implies: the
+    plan targets four rounds of 1024 workgroups, of 64 channels with channels on lanes (at most 256
+    segments unless one round needs more), of 16 otherwise."""
     lib = L.load()
-    args = dict(batch=1, dim=128, dstate=16, seqlen=1 << 20)  # long enough that the layouts' segment counts differ
+    args = dict(batch=1, dim=1024, dstate=16, seqlen=1 << 20)  # long enough that the layouts' segment counts differ
     args.update(kw)
     s = shp(**args)
     Bsz, Dm, N, Ln = args["batch"], args["dim"], args["dstate"], args["seqlen"]
     r = lambda x: (x + 255) // 256 * 256
     cdiv = lambda a, b: -(-a // b)
-    def segments(units, target, cap):
-        seg = max(1024, cdiv(cdiv(Ln, min(cap, cdiv(target, units))), 64) * 64)
+    def segments(units, lanes):
+        want = cdiv(4096, units)
+        if lanes and want > 256:
+            want = max(256, cdiv(1024, units))
+        seg = max(1024, cdiv(cdiv(Ln, want), 64) * 64)
         return cdiv(Ln, seg)
-    S, other = (segments(Bsz * cdiv(Dm, 64), 4096, 256), segments(Bsz * cdiv(Dm, 16), 1024, 1 << 40))[:: 1 if cl else -1]
+    S, other = (segments(Bsz * cdiv(Dm, 64), True), segments(Bsz * cdiv(Dm, 16), False))[:: 1 if cl else -1]
     assert S > 1 and S != other
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * Bsz * Dm * N) + r(4 * (S - 1) * Bsz * Dm)

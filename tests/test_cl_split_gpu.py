@@ -30,7 +30,9 @@ def segments(Bsz, Dm, N, L):
     if not (Bsz * cdiv(Dm, 16) < 512 and 2 * MIN_SEG <= L < 1 << 24 and L % 8 == 0 and N <= 16
             and 5 * (-Dm % 64) <= Dm):
         return None
-    want = min(MAX_SEGMENTS, cdiv(TARGET, Bsz * cdiv(Dm, 64)))
+    want = cdiv(TARGET, Bsz * cdiv(Dm, 64))
+    if want > MAX_SEGMENTS:  # held to 256, or to one round's count if that is more
+        want = max(MAX_SEGMENTS, cdiv(1024, Bsz * cdiv(Dm, 64)))
     seg = max(MIN_SEG, cdiv(cdiv(L, want), 64) * 64)
     return cdiv(L, seg)
 
