@@ -63,7 +63,7 @@ typedef enum ssm_status {
   SSM_ERR_WORKSPACE = 6,   /* workspace non-NULL but smaller than ssm_scan_workspace_size() */
   SSM_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch (hipGetLastError) */
   SSM_ERR_OVERLAP = 8,     /* an output buffer overlaps an input buffer */
-  SSM_ERR_TOO_LARGE = 9    /* ssm_scan_fwd_noalloc: the shape needs more than its 17 MiB of scratch */
+  SSM_ERR_TOO_LARGE = 9    /* ssm_scan_fwd_noalloc: the shape needs more than its 34 MiB of scratch */
 } ssm_status;
 
 typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -138,13 +138,13 @@ ssm_status ssm_scan_fwd_save(const ssm_shape* shape,
 
 /* ssm_scan_fwd for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): it takes no workspace
- * and allocates nothing.  A sequence split uses a scratch array of 17 MiB that the
+ * and allocates nothing.  A sequence split uses a scratch array of 34 MiB that the
  * library holds in static device memory, one copy per GPU, kept until the process
- * ends (it holds the split of 1 x 1024 x 16 x 2^20, bf16, which needs 16.996 MiB);
+ * ends (it holds the split of 1 x 1024 x 16 x 2^20, bf16, which needs 33.996 MiB);
  * its address is looked up once per device, on the first call there.
  *   - Arguments, outputs and errors are those of ssm_scan_fwd, with the split always
- *     enabled; a shape whose split needs more than 17 MiB (ssm_scan_workspace_size()
- *     > 17 MiB) is refused with SSM_ERR_TOO_LARGE before anything is enqueued.
+ *     enabled; a shape whose split needs more than 34 MiB (ssm_scan_workspace_size()
+ *     > 34 MiB) is refused with SSM_ERR_TOO_LARGE before anything is enqueued.
  *   - `stream` must belong to the device whose scratch is used (its own device).
  *   - Every call on one GPU shares that GPU's scratch, which keeps the last call's
  *     contents: calls that overlap in time on one GPU (on different streams, or

@@ -224,12 +224,12 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=N
     return out, final_state
 
 
-SCRATCH_BYTES = 17 << 20  # the static scratch array behind ssm_scan_fwd_noalloc
+SCRATCH_BYTES = 34 << 20  # the static scratch array behind ssm_scan_fwd_noalloc
 
 
 def scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, initial_state=None, *, out, final_state=None,
                      zoh=False, reverse=False, stream=None):
-    """ssm_scan_fwd_noalloc: the selective scan without a workspace; the library's static 17 MiB
+    """ssm_scan_fwd_noalloc: the selective scan without a workspace; the library's static 34 MiB
     per-device scratch array holds a split sequence's segment summaries, and the call allocates
     nothing.  out (and final_state, if given) are the caller's tensors; arguments as scan_fwd.
     Calls that overlap in time on one GPU race on the shared scratch."""

@@ -16,11 +16,12 @@ constexpr int64_t kMaxDim = int64_t(1) << 40;
 constexpr int64_t kMaxElems = int64_t(1) << 61;
 constexpr int kTargetBlocks = 1024;    // output-pass workgroups of 4 waves: 4 per CU on 256 CUs
 constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
-// A split aims at four rounds of output-pass workgroups: shorter segments balance the passes'
-// workgroups over the CUs.  With channels on lanes, at most 256 segments (the carry pass is
-// sequential over them) unless one round needs more.
+// A split aims at several rounds of workgroups: shorter segments balance the passes' workgroups
+// over the CUs.  Four rounds, eight with channels on lanes (whose segments are cheapest to add),
+// there at most 512 segments (the carry pass is sequential over them) unless one round needs more.
 constexpr int kRounds = 4;
-constexpr int64_t kMaxSegmentsCl = 256;
+constexpr int kRoundsCl = 8;
+constexpr int64_t kMaxSegmentsCl = 512;
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -75,7 +76,7 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
              L < (int64_t(1) << 24) && 5 * pad <= s->dim;
     const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;  // workgroups per segment
     const int64_t one = (kTargetBlocks + units - 1) / units;                   // segments for one round
-    int64_t want = (kRounds * kTargetBlocks + units - 1) / units;
+    int64_t want = ((pl->cl ? kRoundsCl : kRounds) * kTargetBlocks + units - 1) / units;
     if (pl->cl && want > kMaxSegmentsCl) want = kMaxSegmentsCl > one ? kMaxSegmentsCl : one;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 63) / 64) * 64;
@@ -175,7 +176,7 @@ const char* ssm_status_str(int status) {
     case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_workspace_size()";
     case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SSM_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
-    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (17 MiB)";
+    case SSM_ERR_TOO_LARGE: return "the call needs more scratch memory than ssm_scan_fwd_noalloc holds (34 MiB)";
     default: return "unknown status";
   }
 }

@@ -115,7 +115,7 @@ hipError_t launch_step(const StepParams& p, bool bf16, hipStream_t s);
 // Size of the static per-device scratch array behind ssm_scan_fwd_noalloc, and its device address
 // on the device `stream` belongs to (the current device for the null stream), looked up once per
 // device.
-constexpr size_t kScratchBytes = size_t(17) << 20;  // holds the split of 1 x 1024 x 16 x 2^20 (bf16)
+constexpr size_t kScratchBytes = size_t(34) << 20;  // holds the split of 1 x 1024 x 16 x 2^20 (bf16)
 hipError_t scratch_buffer(hipStream_t stream, void** ptr);
 
 }  // namespace ssm

@@ -118,25 +118,25 @@ def test_workspace_size_formula():
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, flags=L.SSM_FLAG_ZOH)
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
     # channels on lanes (bf16, default discretisation, N <= 16, L % 8 == 0, L < 2^24): 16 groups
-    # of 64 channels -> 4096 / 16 = 256 segments of 4096 steps (4096 workgroups of the output pass)
+    # of 64 channels -> 8 x 1024 / 16 = 512 segments of 2048 steps (eight rounds of the output pass)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(256)
-    # 4 groups: 1024 segments wanted, held to 256 (one round's count)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(512)
+    # 4 groups: 2048 segments wanted, held to 512
     s = shp(batch=1, dim=256, dstate=16, seqlen=1 << 20)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 256 * 256 * 16) + r(4 * 255 * 256)
-    # 2 groups: 2048 wanted, held to 512, the count of one round (no fewer segments than one round)
-    s = shp(batch=1, dim=128, dstate=16, seqlen=1 << 20)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 512 * 128 * 16) + r(4 * 511 * 128)
-    # 48 groups: 86 segments wanted, of 12224 steps (the last 9536)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 512 * 256 * 16) + r(4 * 511 * 256)
+    # 1 group: 8192 wanted, held to 1024, the count of one round (no fewer segments than one round)
+    s = shp(batch=1, dim=64, dstate=16, seqlen=1 << 20)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * 1024 * 64 * 16) + r(4 * 1023 * 64)
+    # 48 groups: 171 segments wanted, of 6144 steps (the last 4096)
     s = shp(batch=3, dim=1024, dstate=16, seqlen=1 << 20)
-    S = -(-(1 << 20) // ((-(-(1 << 20) // 86) + 63) // 64 * 64))
-    assert S == 86
+    S = -(-(1 << 20) // ((-(-(1 << 20) // 171) + 63) // 64 * 64))
+    assert S == 171
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * 3 * 1024 * 16) + r(4 * (S - 1) * 3 * 1024)
     # D = 1000 pads 24 channels to whole groups (under a fifth): still channels on lanes; D = 100
     # would pad 28 (over a fifth) and L not a multiple of 8 breaks the 16-byte rows: lanes over states
     s = shp(batch=1, dim=1000, dstate=16, seqlen=1 << 20)
     b1, b2 = 1000 * 16, 1000
-    S = 256  # 16 groups
+    S = 512  # 16 groups
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=100, dstate=16, seqlen=1 << 16)
     S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 586 segments wanted, held to 1024 steps each
@@ -322,7 +322,7 @@ def test_saved_checkpoint_entry_points():
 
 def test_noalloc_errors_before_any_launch():
     """ssm_scan_fwd_noalloc checks every argument on the host first, then its scratch limit (a
-    split that needs more than its 17 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
+    split that needs more than its 34 MiB: SSM_ERR_TOO_LARGE); none of these reach the GPU."""
     lib = L.load()
 
     def call(shape, **kw):
@@ -331,8 +331,8 @@ def test_noalloc_errors_before_any_launch():
         return lib.ssm_scan_fwd_noalloc(None if shape is None else ctypes.byref(shape), p["u"], p["delta"], p["A"],
                                         p["B"], p["C"], None, None, None, None, p["out"], None, None)
 
-    # 1 x 1152 x 16 x 2^20: 18 groups of 64 channels, 228 segments, 17.03 MiB; the DNA shape
-    # (1 x 1024 x 16 x 2^20, 256 segments) needs 16.996 MiB and fits
+    # 1 x 1152 x 16 x 2^20: 18 groups of 64 channels, 456 segments, 34.06 MiB; the DNA shape
+    # (1 x 1024 x 16 x 2^20, 512 segments) needs 33.996 MiB and fits
     big = shp(batch=1, dim=1152, dstate=16, seqlen=1 << 20)
     assert L.load().ssm_scan_workspace_size(ctypes.byref(big)) > L.SCRATCH_BYTES
     dna = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
@@ -360,8 +360,8 @@ def test_noalloc_errors_before_any_launch():
 ], ids=["base", "N17", "zoh", "fp32", "L_not_8", "pad_over_fifth", "pad_a_fifth", "reverse"])
 def test_split_layout_rule(kw, cl):
     """Which layout the split's passes take, read from the segment count the workspace implies: the
-    plan targets four rounds of 1024 workgroups, of 64 channels with channels on lanes (at most 256
-    segments unless one round needs more), of 16 otherwise."""
+    plan targets eight rounds of 1024 workgroups of 64 channels with channels on lanes (at most 512
+    segments unless one round needs more), four rounds of 16-channel workgroups otherwise."""
     lib = L.load()
     args = dict(batch=1, dim=1024, dstate=16, seqlen=1 << 20)  # long enough that the layouts' segment counts differ
     args.update(kw)
@@ -370,9 +370,9 @@ def test_split_layout_rule(kw, cl):
     r = lambda x: (x + 255) // 256 * 256
     cdiv = lambda a, b: -(-a // b)
     def segments(units, lanes):
-        want = cdiv(4096, units)
-        if lanes and want > 256:
-            want = max(256, cdiv(1024, units))
+        want = cdiv(8192 if lanes else 4096, units)
+        if lanes and want > 512:
+            want = max(512, cdiv(1024, units))
         seg = max(1024, cdiv(cdiv(Ln, want), 64) * 64)
         return cdiv(Ln, seg)
     S, other = (segments(Bsz * cdiv(Dm, 64), True), segments(Bsz * cdiv(Dm, 16), False))[:: 1 if cl else -1]

@@ -16,7 +16,7 @@ from tests.test_parity_gpu import full_check, make
 
 pytestmark = pytest.mark.gpu
 
-MIN_SEG, TARGET, MAX_SEGMENTS = 1024, 4096, 256
+MIN_SEG, TARGET, MAX_SEGMENTS = 1024, 8192, 512
 
 
 def cdiv(a, b):
@@ -31,7 +31,7 @@ def segments(Bsz, Dm, N, L):
             and 5 * (-Dm % 64) <= Dm):
         return None
     want = cdiv(TARGET, Bsz * cdiv(Dm, 64))
-    if want > MAX_SEGMENTS:  # held to 256, or to one round's count if that is more
+    if want > MAX_SEGMENTS:  # held to 512, or to one round's count if that is more
         want = max(MAX_SEGMENTS, cdiv(1024, Bsz * cdiv(Dm, 64)))
     seg = max(MIN_SEG, cdiv(cdiv(L, want), 64) * 64)
     return cdiv(L, seg)

@@ -39,7 +39,7 @@ CASES = [
     ("bf16 ZOH split with h0 then smaller", torch.bfloat16, (1, 24, 16, 8192), (1, 8, 16, 2048), {"zoh": True}),
     ("bf16 channels-on-lanes split then smaller, reverse", torch.bfloat16, (1, 128, 16, 8192), (2, 64, 16, 4096),
      {"reverse": True}),
-    ("bf16 1 x 1024 x 16 x 2^20 (256 segments) then smaller", torch.bfloat16, (1, 1024, 16, 1 << 20),
+    ("bf16 1 x 1024 x 16 x 2^20 (512 segments) then smaller", torch.bfloat16, (1, 1024, 16, 1 << 20),
      (1, 64, 16, 4096), {}),
 ]
 
