@@ -16,11 +16,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 40;
 constexpr int64_t kMaxElems = int64_t(1) << 61;
 constexpr int kTargetBlocks = 1024;    // output-pass workgroups of 4 waves: 4 per CU on 256 CUs
 constexpr int64_t kMinSegment = 1024;  // shortest segment worth a summary pass
-// A split aims at several rounds of workgroups: shorter segments balance the passes' workgroups
-// over the CUs.  Four rounds, eight with channels on lanes (whose segments are cheapest to add),
-// there at most 512 segments (the carry pass is sequential over them) unless one round needs more.
-constexpr int kRounds = 4;
-constexpr int kRoundsCl = 8;
+// A split aims at eight rounds of workgroups: shorter segments balance the passes' workgroups over
+// the CUs.  With channels on lanes at most 512 segments (the carry pass is sequential over them)
+// unless one round needs more.
+constexpr int kRounds = 8;
 constexpr int64_t kMaxSegmentsCl = 512;
 
 struct Range {
@@ -76,7 +75,7 @@ bool make_plan(const ssm_shape* s, Plan* pl) {
              L < (int64_t(1) << 24) && 5 * pad <= s->dim;
     const int64_t units = pl->cl ? s->batch * ((s->dim + 63) / 64) : base;  // workgroups per segment
     const int64_t one = (kTargetBlocks + units - 1) / units;                   // segments for one round
-    int64_t want = ((pl->cl ? kRoundsCl : kRounds) * kTargetBlocks + units - 1) / units;
+    int64_t want = (kRounds * kTargetBlocks + units - 1) / units;
     if (pl->cl && want > kMaxSegmentsCl) want = kMaxSegmentsCl > one ? kMaxSegmentsCl : one;
     int64_t seg = (L + want - 1) / want;
     seg = ((seg + 63) / 64) * 64;
@@ -112,7 +111,7 @@ constexpr int kBwdTargetBlocks = 768;  // 3 backward workgroups per CU on 256 CU
 
 // Shape-only, like the forward's plan.  Few channels and a long sequence: split the sequence
 // into segments (whole 256-step chunks, >= 1024 steps) so that about kRounds x kBwdTargetBlocks
-// workgroups run (four rounds); each segment's checkpoints start from a carried state (summary
+// workgroups run (eight rounds); each segment's checkpoints start from a carried state (summary
 // pass + carry) and its adjoint from a carried adjoint (adjoint summary + carry).
 bool make_bwd_plan(const ssm_shape* s, BwdPlan* pl, bool saved = false) {
   Plan fp;

@@ -111,12 +111,12 @@ def test_workspace_size_formula():
     r = lambda x: (x + 255) // 256 * 256
     # carries [S,B,D,N] (segment end states written into them in place) + step-size sums [S-1,B,D]
     want = lambda S: r(4 * S * bdn) + r(4 * (S - 1) * bd)
-    # lanes over states (fp32 streams, or ZOH): 64 channel blocks of 16 -> 4 x 1024 / 64 = 64 segments
-    # of 16384 steps (four rounds of output-pass workgroups)
+    # lanes over states (fp32 streams, or ZOH): 64 channel blocks of 16 -> 8 x 1024 / 64 = 128 segments
+    # of 8192 steps (eight rounds of output-pass workgroups)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, io_dtype=L.SSM_F32)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(128)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20, flags=L.SSM_FLAG_ZOH)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(128)
     # channels on lanes (bf16, default discretisation, N <= 16, L % 8 == 0, L < 2^24): 16 groups
     # of 64 channels -> 8 x 1024 / 16 = 512 segments of 2048 steps (eight rounds of the output pass)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=1 << 20)
@@ -139,16 +139,16 @@ def test_workspace_size_formula():
     S = 512  # 16 groups
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=100, dstate=16, seqlen=1 << 16)
-    S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 586 segments wanted, held to 1024 steps each
+    S = (1 << 16) // 1024  # 7 channel blocks of 16 -> 1171 segments wanted, held to 1024 steps each
     b1, b2 = 100 * 16, 100
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
     s = shp(batch=1, dim=1024, dstate=16, seqlen=(1 << 20) - 4)
-    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(64)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == want(128)
     # 2^24 steps: 64 rows of a stream pass 2^31 bytes, lanes over states (4 blocks of 16 channels
-    # -> 1024 segments of 16384 steps)
+    # -> 2048 segments of 8192 steps)
     s = shp(batch=1, dim=64, dstate=16, seqlen=1 << 24)
     b1, b2 = 64 * 16, 64
-    S = 1024
+    S = 2048
     assert lib.ssm_scan_workspace_size(ctypes.byref(s)) == r(4 * S * b1) + r(4 * (S - 1) * b2)
 
 
@@ -360,8 +360,8 @@ def test_noalloc_errors_before_any_launch():
 ], ids=["base", "N17", "zoh", "fp32", "L_not_8", "pad_over_fifth", "pad_a_fifth", "reverse"])
 def test_split_layout_rule(kw, cl):
     """Which layout the split's passes take, read from the segment count the workspace implies: the
-    plan targets eight rounds of 1024 workgroups of 64 channels with channels on lanes (at most 512
-    segments unless one round needs more), four rounds of 16-channel workgroups otherwise."""
+    plan targets eight rounds of 1024 workgroups, of 64 channels with channels on lanes (at most 512
+    segments unless one round needs more), of 16 otherwise."""
     lib = L.load()
     args = dict(batch=1, dim=1024, dstate=16, seqlen=1 << 20)  # long enough that the layouts' segment counts differ
     args.update(kw)
@@ -370,7 +370,7 @@ def test_split_layout_rule(kw, cl):
     r = lambda x: (x + 255) // 256 * 256
     cdiv = lambda a, b: -(-a // b)
     def segments(units, lanes):
-        want = cdiv(8192 if lanes else 4096, units)
+        want = cdiv(8192, units)
         if lanes and want > 512:
             want = max(512, cdiv(1024, units))
         seg = max(1024, cdiv(cdiv(Ln, want), 64) * 64)
