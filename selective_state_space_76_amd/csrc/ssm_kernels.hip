@@ -73,6 +73,53 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanParams p) {
   }
 }
 
+// The same chain over at most 32 x GR segments, in two levels: a workgroup holds CW = 1024 / GR
+// consecutive (b, d, n) chains and GR groups of K consecutive segments; thread (group, chain) folds
+// its segments into (P, Q) = (product of the decays, state reached from zero), the groups' pairs go
+// through LDS, each thread composes the groups to its left (in order) with the initial state and
+// reruns its own segments, writing their carries.  Every summary a workgroup reads is loaded and
+// used by the fold before the barrier, and every carry is stored after it, so this also runs in
+// place.
+template <int K, int GR>
+__global__ __launch_bounds__(1024) void carry_tree_kernel(ScanParams p) {
+  constexpr int CW = 1024 / GR;
+  __shared__ float sp[GR][CW], sq[GR][CW];
+  const int c = threadIdx.x % CW, gr = threadIdx.x / CW;
+  const int64_t BDN = p.Bsz * p.Dm * p.N;
+  const int64_t idx = (int64_t)blockIdx.x * CW + c;
+  const bool v = idx < BDN;
+  const int64_t ix = v ? idx : 0;
+  const int64_t n = ix % p.N, bd = ix / p.N, d = bd % p.Dm;
+  const float Ap = p.A[d * p.N + n] * kLog2e;
+  const int s0 = gr * K;
+  float st[K], dec[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {  // the last segment has no summary: an identity step
+    const int s = s0 + k;
+    const bool has = s + 1 < p.S;
+    st[k] = has ? p.seg_state[(int64_t)s * BDN + ix] : 0.0f;
+    const float ds = has ? p.seg_dsum[(int64_t)s * p.Bsz * p.Dm + bd] : 0.0f;
+    dec[k] = has ? exp2_(Ap * ds) : 1.0f;
+  }
+  float P = 1.0f, Q = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    Q = __builtin_fmaf(dec[k], Q, st[k]);
+    P *= dec[k];
+  }
+  sp[gr][c] = P;
+  sq[gr][c] = Q;
+  __syncthreads();
+  float hc = (v && p.init) ? p.init[ix] : 0.0f;
+  for (int j = 0; j < gr; ++j) hc = __builtin_fmaf(sp[j][c], hc, sq[j][c]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int s = s0 + k;
+    if (v && s < p.S) p.carries[(int64_t)s * BDN + ix] = hc;
+    hc = __builtin_fmaf(dec[k], hc, st[k]);
+  }
+}
+
 hipError_t launch_scan_f32_out(const ScanParams& p, int grid, hipStream_t s);
 hipError_t launch_scan_f32_sum(const ScanParams& p, int grid, hipStream_t s);
 hipError_t launch_scan_bf16_out(const ScanParams& p, int grid, hipStream_t s);
@@ -85,9 +132,22 @@ hipError_t launch_scan(const ScanParams& p, bool bf16, int mode, hipStream_t s) 
   return mode == 0 ? launch_scan_f32_out(p, grid, s) : launch_scan_f32_sum(p, grid, s);
 }
 
+template <int K, int GR>
+static void launch_carry_tree(const ScanParams& p, hipStream_t s) {
+  constexpr int CW = 1024 / GR;
+  const int64_t BDN = p.Bsz * p.Dm * p.N;
+  hipLaunchKernelGGL((carry_tree_kernel<K, GR>), dim3((unsigned)((BDN + CW - 1) / CW)), dim3(1024), 0, s, p);
+}
+
 hipError_t launch_carry(const ScanParams& p, hipStream_t s) {
   const int64_t BDN = p.Bsz * p.Dm * p.N;
-  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((BDN + 255) / 256)), dim3(256), 0, s, p);
+  // two levels up to 1024 segments (each thread's segments in registers); a chain per thread beyond
+  if (p.S <= 64) launch_carry_tree<4, 16>(p, s);
+  else if (p.S <= 128) launch_carry_tree<8, 16>(p, s);
+  else if (p.S <= 256) launch_carry_tree<16, 16>(p, s);
+  else if (p.S <= 512) launch_carry_tree<32, 16>(p, s);
+  else if (p.S <= 1024) launch_carry_tree<32, 32>(p, s);
+  else hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((BDN + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from selective_state_space_76_amd import scan_fwd, state_update, workspace_size
+from selective_state_space_76_amd import SSM_F32, scan_fwd, state_update, workspace_size
 from selective_state_space_76_amd import workloads as W
 from tests.gpu_util import check_bf16_ulp, oracle_rows, rel_err, sample_rows, tol_for
 
@@ -96,6 +96,19 @@ def test_split_path(L):
 def test_split_path_fp32_wide_state():
     print("case: split fp32 N=64", flush=True)
     full_check(make(1, 16, 64, 3000, dtype=torch.float32, seed=11))
+
+
+@pytest.mark.parametrize("L", [40000, 100000, 200000, 450000, 1000000, 1500000])
+def test_split_segment_counts(L):
+    """Few channels, very long sequences: with one segment per 1024 steps here (40 to 1465 segments)
+    the carry pass runs in each of its forms -- two levels with 4, 8, 16 or 32 segments per thread
+    and 16 or 32 groups, and one chain per (channel, state) beyond 1024 segments -- from an initial
+    state."""
+    print("case: split segment count, fp32 1x3x5x%d" % L, flush=True)
+    x = make(1, 3, 5, L, dtype=torch.float32, seed=L % 997)
+    assert workspace_size(1, 3, 5, L, SSM_F32) > 4 * 15 * (L // 1024)  # the carries of every segment
+    h0 = torch.randn(1, 3, 5, generator=torch.Generator().manual_seed(13))
+    full_check(x, h0=h0)
 
 
 @pytest.mark.parametrize("name", ["mamba130m", "mamba1p3b", "dna1m"])
