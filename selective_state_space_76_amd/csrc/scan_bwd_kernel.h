@@ -190,9 +190,15 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
   constexpr int PPT = 2 * 16 * PPR / 256;     // B and C pieces per thread (16 states)
   // [tensor][state of the stage][float4 group][lane]: step 16 lane + 4 group + component
   __shared__ f32x4 bc[2 * 16 * KG * 16];
+  // The default discretisation with 8 steps per lane runs only up to 32 states (more take 16 steps per
+  // lane), so its per-state constants need half the LDS; it keeps u and the dz factor of its steps,
+  // which the loop over states does not read, in the LDS that frees instead of in registers.
+  constexpr bool STASH = T == 8 && !ZOH;
+  constexpr int NM = STASH ? 32 : 64;         // states the per-state LDS arrays hold
   // [channel of the workgroup][state]: A log2(e), A, 1/A (ZOH), adjoint entering the chunk from the right
-  __shared__ float4 cst[16 * 64];
-  __shared__ float dacc[16 * 64];             // [channel][state]: dA summed over the steps done so far
+  __shared__ float4 cst[16 * NM];
+  __shared__ float dacc[16 * NM];             // [channel][state]: dA summed over the steps done so far
+  __shared__ float stash[STASH ? 2 * T * 256 : 1];  // [value][step][thread]: u, dz factor
   __shared__ float red[2][4][2 * CH];         // [parity][wave][dB | dC of the chunk's steps]
   __shared__ float hck[16 * 16];              // [channel][state of the stage]: state entering the chunk
 
@@ -213,11 +219,11 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
   const bool has_z = p.z != nullptr;
   const float biasd = p.bias ? p.bias[dd] : 0.0f;
   const float Dd = p.D ? p.D[dd] : 0.0f;
-  float4* cs = cst + cl * 64;
-  float* da = dacc + cl * 64;
+  float4* cs = cst + cl * NM;
+  float* da = dacc + cl * NM;
 
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < NM / 16; ++k) {
     const int64_t n = g + 16 * k;
     if (n < N) {
       const float a = p.A[dd * N + n];
@@ -280,6 +286,10 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
         if (tv) dDacc = __builtin_fmaf(dy[s], fu[e], dDacc);
         if (s < T / 2) cumlo += dts;
         else cumhi += dts;
+        if constexpr (STASH) {  // read back by this thread alone, after the loop over states
+          stash[s * 256 + tid] = uu[s];
+          stash[(T + s) * 256 + tid] = dzf[s];
+        }
       }
     }
 
@@ -460,6 +470,10 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
       for (int e = 0; e < EPC; ++e) {
         const int s = k * EPC + e;
         const int64_t t = t0 + s;
+        if constexpr (STASH) {
+          uu[s] = stash[s * 256 + tid];
+          dzf[s] = stash[(T + s) * 256 + tid];
+        }
         const float du = ZOH ? __builtin_fmaf(dy[s], Dd, S1[s]) : __builtin_fmaf(dy[s], Dd, dt[s] * S1[s]);
         const float ddt = ZOH ? S2[s] : __builtin_fmaf(uu[s], S1[s], S2[s]);
         const float ddl = ddt * softplus_slope(dt[s]);
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
 
   if (dval) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NM / 16; ++k) {
       const int64_t n = g + 16 * k;
       if (n < N) {
         p.part_a[(((int64_t)seg * p.Bsz + b) * Dm + d) * N + n] = da[n];
