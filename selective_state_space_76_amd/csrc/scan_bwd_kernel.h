@@ -237,13 +237,10 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
     }
   }
 
-  const IO* urow = reinterpret_cast<const IO*>(p.u) + (b * Dm + dd) * L;
-  const IO* drow = reinterpret_cast<const IO*>(p.delta) + (b * Dm + dd) * L;
-  const IO* zrow = has_z ? reinterpret_cast<const IO*>(p.z) + (b * Dm + dd) * L : nullptr;
-  const IO* grow = reinterpret_cast<const IO*>(p.dout) + (b * Dm + dd) * L;
-  IO* du_row = reinterpret_cast<IO*>(p.du) + (b * Dm + dd) * L;
-  IO* dd_row = reinterpret_cast<IO*>(p.ddelta) + (b * Dm + dd) * L;
-  IO* dz_row = has_z ? reinterpret_cast<IO*>(p.dz) + (b * Dm + dd) * L : nullptr;
+  // The seven [B, D, L] streams share this lane's row offset.  Their row pointers are formed from it
+  // where they are used (an empty asm hides the offset from loop-invariant hoisting), so the lane keeps
+  // one 64-bit offset through the loop over states instead of seven pointers.
+  const int64_t roff0 = (b * Dm + dd) * L;
   float dDacc = 0.0f, dbacc = 0.0f;  // this lane's dD and dbias terms
   int par = 0;                       // parity of the dB/dC exchange buffer
   // the segment's chunks (a split segment is a whole number of chunks; the last one may be ragged)
@@ -254,6 +251,12 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
   for (int64_t ci = nch - 1; ci >= 0; --ci) {
     const int64_t c0 = tb + ci * CH;
     const int64_t t0 = c0 + g * T;
+    int64_t roff = roff0;
+    asm volatile("" : "+v"(roff));
+    const IO* urow = reinterpret_cast<const IO*>(p.u) + roff;
+    const IO* drow = reinterpret_cast<const IO*>(p.delta) + roff;
+    const IO* zrow = has_z ? reinterpret_cast<const IO*>(p.z) + roff : nullptr;
+    const IO* grow = reinterpret_cast<const IO*>(p.dout) + roff;
 
     // per-(channel, step) values of this lane's 16 steps
     float dt[T], uu[T], xu[T], dy[T], dzf[T];
@@ -464,6 +467,11 @@ __global__ __launch_bounds__(256, T == 16 ? 2 : 3) void scan_bwd_kernel(BwdParam
     }
 
     // per-step outputs of this lane's steps
+    int64_t roffo = roff0;
+    asm volatile("" : "+v"(roffo));
+    IO* du_row = reinterpret_cast<IO*>(p.du) + roffo;
+    IO* dd_row = reinterpret_cast<IO*>(p.ddelta) + roffo;
+    IO* dz_row = has_z ? reinterpret_cast<IO*>(p.dz) + roffo : nullptr;
 #pragma unroll
     for (int k = 0; k < T / EPC; ++k) {
 #pragma unroll
