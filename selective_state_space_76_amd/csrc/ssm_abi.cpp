@@ -245,7 +245,9 @@ ssm_status scan_fwd_impl(const ssm_shape* shape, const void* u, const void* delt
   p.init = initial_state; p.out = out; p.final_state = final_state; p.ckpt = ckpt;
   p.Bsz = Bsz; p.Dm = Dm; p.N = N; p.L = L;
   p.nblk = (int)pl.nblk;
-  p.vec = (L % (16 / es)) == 0 && L >= 8 ? 1 : 0;  // 16-byte chunks stay inside each row
+  // 16-byte chunks stay inside each row; the whole-chunk staging's buffer resources span 8 rows of L
+  // elements, so longer rows take the element path
+  p.vec = (L % (16 / es)) == 0 && L >= 8 && L < (int64_t(1) << 24) ? 1 : 0;
   p.reverse = (shape->flags & SSM_FLAG_REVERSE) ? 1 : 0;
   p.zoh = (shape->flags & SSM_FLAG_ZOH) ? 1 : 0;
   const bool bf16 = shape->io_dtype == SSM_BF16;
@@ -434,7 +436,7 @@ ssm_status scan_bwd_impl(const ssm_shape* shape, const void* u, const void* delt
     fp.S = (int)pl.S;
     fp.seg_len = split ? pl.seg_len : pl.nbk * 64;
     fp.nblk = (int)pl.nblk;
-    fp.vec = vec;
+    fp.vec = vec && L < (int64_t(1) << 24) ? 1 : 0;  // the scan kernel's whole-chunk staging (above)
     fp.reverse = rev;
     fp.zoh = zoh;
     if (split) {

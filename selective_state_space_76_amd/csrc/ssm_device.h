@@ -193,7 +193,7 @@ __device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
 // states (rows >= N stay zero) and delta/u/z of its 16 channels, all fetched
 // with coalesced 16-byte loads one block ahead into registers.
 template <typename IO, int NL, int MODE, bool ZOH, bool REV, bool VEC>
-__global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2) void scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : (NL == 4 && !ZOH && sizeof(IO) == 2 ? 3 : 2)) : 2) void scan_kernel(ScanParams p) {
   constexpr int NP = 16 * NL;                  // states padded to the lane grid
   constexpr int TS = 68;                       // LDS tile row: 64 steps + 4 pad (floats)
   constexpr int NT = MODE == 0 ? 2 : 1;        // staged coefficient tensors: B and C, or B only
@@ -283,44 +283,101 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
     }
   }
 
-  // Blocks wholly inside the rows (16-byte rows): unconditional loads from addresses that are valid
-  // for every chunk slot (slots that are not live are never stored, so what they load is unused).
-  const IO* fsrc[CPT];
+  // Rows of whole 16-byte pieces (VEC): every region of the chunk slots (B, C, each channel stream) is a
+  // whole number of 64-slot groups, so wave w's chunk k -- slots 256 k + 64 w + lane -- lies in one
+  // tensor and covers RPC consecutive rows of it (lane: row lane / CPR, piece lane % CPR).  Each such
+  // chunk reads through a buffer resource over its valid rows, so rows past N or D read zero, every
+  // chunk of a lane takes the same 32-bit lane offset, and the block's step offset is a scalar.  The
+  // host keeps L below 2^24 on this path (each resource spans RPC rows of L elements).
+  constexpr int RPC = 64 / CPR;
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  const int lrow = lane / CPR, lcol = (lane % CPR) * EPC;
+  __amdgpu_buffer_rsrc_t rs[CPT];
+  int dbase[CPT];
+  bool wok[CPT];
+  uint32_t voff = 0;
+  if constexpr (VEC) {
 #pragma unroll
-  for (int k = 0; k < CPT; ++k)
-    fsrc[k] = (src[k] ? src[k] : reinterpret_cast<const IO*>(p.u)) + (REV ? (L - EPC - col[k]) : col[k]);
+    for (int k = 0; k < CPT; ++k) {
+      const int c0 = 256 * k + 64 * wv;  // the chunk's first slot
+      const void* base = p.u;
+      int64_t rows = 0;
+      dbase[k] = 0;
+      wok[k] = c0 < NCH;
+      if (c0 < NBC) {
+        const int tt = c0 / (NP * CPR), n0 = (c0 / CPR) % NP;
+        if (n0 < N) {
+          base = reinterpret_cast<const IO*>(tt == 0 ? p.B : p.C) + (b * N + n0) * L;
+          rows = N - n0 < RPC ? N - n0 : RPC;
+        }
+        dbase[k] = (tt * NP + n0) * TS;
+      } else if (c0 < NCH) {
+        const int e = c0 - NBC;
+        const int st = e / (16 * CPR), row0 = (e / CPR) % 16;
+        const int64_t dr0 = (int64_t)cb * 16 + row0;
+        const void* sb = st == 0 ? p.delta : (st == 1 ? p.u : p.z);
+        if (sb != nullptr && dr0 < Dm) {
+          base = reinterpret_cast<const IO*>(sb) + (b * Dm + dr0) * L;
+          rows = Dm - dr0 < RPC ? Dm - dr0 : RPC;
+        }
+        dbase[k] = NT * NP * TS + (st * 16 + row0) * TS;
+      }
+      rs[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                (int)(rows * L * (int64_t)sizeof(IO)), 0x00020000);
+    }
+    // lane offset in bytes: forward, row + piece + t0; backward in time, row + (L - EPC - piece) - t0,
+    // taken as (row + 64 - EPC - piece) + (L - 64 - t0) for whole blocks
+    voff = (uint32_t)(((int64_t)lrow * L + (REV ? 64 - EPC - lcol : lcol)) * (int64_t)sizeof(IO));
+  }
+  auto vload = [&](int k, uint32_t vo, int so) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs[k], vo, so, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+
+  // Other rows: element loads with bounds checks, through the chunks' row pointers.
   uint4 raw[CPT];
   auto fetch = [&](int64_t t0) {
-    if (VEC && t0 + 64 <= L) {
+    if constexpr (VEC) {
+      if (t0 + 64 <= L) {  // the whole block lies inside the rows
+        const int so = (int)((REV ? L - 64 - t0 : t0) * (int64_t)sizeof(IO));
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) raw[k] = *reinterpret_cast<const uint4*>(fsrc[k] + (REV ? -t0 : t0));
+        for (int k = 0; k < CPT; ++k)
+          if (wok[k]) raw[k] = vload(k, voff, so);
+        return;
+      }
+      // the sequence's ragged last block: pieces at or past L hold zero
+      const int64_t ts = t0 + lcol;
+      const uint32_t vr = (uint32_t)(((int64_t)lrow * L + (REV ? L - EPC - ts : ts)) * (int64_t)sizeof(IO));
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        raw[k] = make_uint4(0, 0, 0, 0);
+        if (wok[k] && ts < L) raw[k] = vload(k, vr, 0);
+      }
       return;
-    }
+    } else {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int64_t ts = t0 + col[k];  // first logical step of the chunk
       uint4 v = make_uint4(0, 0, 0, 0);
       if (live[k] && ts < L) {
-        if (VEC) {
-          v = *reinterpret_cast<const uint4*>(src[k] + (REV ? (L - EPC - ts) : ts));
-        } else {
-          IO e[EPC];
+        IO e[EPC];
 #pragma unroll
-          for (int k2 = 0; k2 < EPC; ++k2) {
-            // physical order inside the chunk matches the vector path
-            const int64_t lt = REV ? (ts + EPC - 1 - k2) : (ts + k2);
-            e[k2] = (lt < L) ? src[k][REV ? (L - 1 - lt) : lt] : IO(0);
-          }
-          v = *reinterpret_cast<const uint4*>(e);
+        for (int k2 = 0; k2 < EPC; ++k2) {
+          // physical order inside the chunk matches the vector path
+          const int64_t lt = REV ? (ts + EPC - 1 - k2) : (ts + k2);
+          e[k2] = (lt < L) ? src[k][REV ? (L - 1 - lt) : lt] : IO(0);
         }
+        v = *reinterpret_cast<const uint4*>(e);
       }
       raw[k] = v;
+    }
     }
   };
   auto store = [&](float* tile) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      if (live[k]) {
+      const bool go = VEC ? wok[k] : live[k];
+      if (go) {
         float f[EPC];
         if constexpr (sizeof(IO) == 2) {
           const uint32_t x[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
@@ -333,12 +390,13 @@ __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : 2) : 2)
           f[0] = __uint_as_float(raw[k].x); f[1] = __uint_as_float(raw[k].y);
           f[2] = __uint_as_float(raw[k].z); f[3] = __uint_as_float(raw[k].w);
         }
+        float* dp = tile + (VEC ? dbase[k] + lrow * TS + lcol : dst[k]);
 #pragma unroll
         for (int k2 = 0; k2 < EPC; k2 += 4) {
           float4 o;
           if (REV) o = make_float4(f[EPC - 1 - k2], f[EPC - 2 - k2], f[EPC - 3 - k2], f[EPC - 4 - k2]);
           else o = make_float4(f[k2], f[k2 + 1], f[k2 + 2], f[k2 + 3]);
-          *reinterpret_cast<float4*>(tile + dst[k] + k2) = o;
+          *reinterpret_cast<float4*>(dp + k2) = o;
         }
       }
     }
