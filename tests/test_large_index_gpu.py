@@ -128,3 +128,25 @@ def test_conv_update_past_2_31_state_elements():
         es = rel_err(st[b:b + 1, d:d + 1], rs)
         assert eu <= TOL and es <= TOL, ((b, d), eu, es)
     print("conv update sampled rows within %g" % TOL, flush=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_rows_of_2_24_steps_or_more(dtype):
+    """Rows of 2^24 steps or more take the scan's element-load staging (the whole-piece staging's buffer
+    resources span 8 rows of L elements, so the library keeps it below 2^24), through the sequence split,
+    in both directions; every element is compared with the oracle."""
+    L = (1 << 24) + 64
+    name = "tiny" if dtype == torch.float32 else "mamba130m"
+    w = W.WORKLOADS[name].with_shape(batch=1, dim=2, dstate=4, seqlen=L, seed=9200)
+    x = W.scan_inputs(w)
+    tol = 1e-4 if dtype == torch.float32 else TOL
+    for rev in (False, True):
+        print("case: rows of 2^24 + 64 steps, %s, reverse=%s" % (dtype, rev), flush=True)
+        g = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+        out, fs = scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"], reverse=rev)
+        torch.cuda.synchronize()
+        ref_y, ref_h = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                                   delta_bias=x["delta_bias"], reverse=rev)
+        ey, eh = rel_err(out, ref_y), rel_err(fs, ref_h)
+        print("rel_err y=%.3g state=%.3g" % (ey, eh), flush=True)
+        assert ey <= tol and eh <= tol
