@@ -187,11 +187,14 @@ __device__ __forceinline__ float row_transpose_sum(const float (&v)[16]) {
 // MODE 2: checkpoint pass for the backward (writes the state entering every
 //         64-step block to ckpt; a split sequence starts each segment from its carry).
 // REV: logical step t reads physical position L-1-t.  VEC: rows allow 16-byte
-// vector loads (L a multiple of 8 for bf16, of 4 for fp32, and L >= 8).
+// vector loads (L a multiple of 8 for bf16, of 4 for fp32, 8 <= L < 2^24).
 //
 // Per 64-step block the workgroup stages, as fp32 in LDS, B (and C) for all
 // states (rows >= N stay zero) and delta/u/z of its 16 channels, all fetched
 // with coalesced 16-byte loads one block ahead into registers.
+// Waves per SIMD the output pass is built for: 4 with one state per lane (3 with
+// ZOH), 3 with 64 bf16 states (168 VGPRs, which the buffer-resource staging below
+// leaves room for), 2 otherwise.
 template <typename IO, int NL, int MODE, bool ZOH, bool REV, bool VEC>
 __global__ __launch_bounds__(256, MODE == 0 ? (NL == 1 ? (ZOH ? 3 : 4) : (NL == 4 && !ZOH && sizeof(IO) == 2 ? 3 : 2)) : 2) void scan_kernel(ScanParams p) {
   constexpr int NP = 16 * NL;                  // states padded to the lane grid

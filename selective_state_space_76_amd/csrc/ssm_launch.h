@@ -27,7 +27,7 @@ struct ScanParams {
   int64_t seg_len;       // steps per segment, a multiple of 64
   int S;                 // number of segments (1: no split)
   int nblk;              // channel blocks of 16 = ceil(Dm / 16)
-  int vec;               // rows allow 16-byte vector loads
+  int vec;               // rows of whole 16-byte pieces, shorter than 2^24 elements (the scan's whole-piece staging)
   int reverse;           // scan from the last step to the first
   int zoh;               // zero-order-hold B_bar
 };
